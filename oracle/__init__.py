@@ -1,0 +1,140 @@
+"""ctypes loader for the FP64 CPU oracle in ``mhcpb_oracle.c``.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark use it; the GPU library never does.  It follows the
+formula of the "DSv4.1 mHC projection/RMS backward" cuDNN Frontend page
+(introduction):  P = grad_proj[:, :24], dX = P W + grad_r / (r K) X,
+dW = P^T X, with TF32 operands in ``mode="tf32"`` and exact FP32 operands in
+``mode="exact"``; results are FP64 with no final rounding.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mhcpb_oracle.c")
+_LIB = os.path.join(_HERE, "libmhcpb_oracle.so")
+
+_MODES = {"exact": 0, "tf32": 1}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into oracle/libmhcpb_oracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+             "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"],
+            check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        i64 = ctypes.c_int64
+        lib.oracle_tf32.argtypes = [ctypes.c_float]
+        lib.oracle_tf32.restype = ctypes.c_double
+        lib.oracle_bf16.argtypes = [ctypes.c_float]
+        lib.oracle_bf16.restype = ctypes.c_float
+        lib.oracle_dx.argtypes = [ctypes.c_int, i64, i64, i64, f32p, f32p, f32p,
+                                  f32p, f32p, u16p, f64p]
+        lib.oracle_dx.restype = ctypes.c_int
+        lib.oracle_dw.argtypes = [ctypes.c_int, i64, i64, f32p, f32p, f64p]
+        lib.oracle_dw.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def tf32(v: float) -> float:
+    """TF32 value (round-to-nearest-even of the fraction to 10 bits)."""
+    return _load().oracle_tf32(float(np.float32(v)))
+
+
+def tf32_array(a) -> np.ndarray:
+    """Elementwise TF32 values of an FP32 array, as float64."""
+    lib = _load()
+    flat = np.ascontiguousarray(a, dtype=np.float32).ravel()
+    out = np.array([lib.oracle_tf32(float(v)) for v in flat], dtype=np.float64)
+    return out.reshape(np.shape(a))
+
+
+def bf16(v: float) -> np.float32:
+    """BF16 value (round to nearest even) of an FP32 value, as float32."""
+    return np.float32(_load().oracle_bf16(float(np.float32(v))))
+
+
+def bf16_bits(v: float) -> int:
+    """The 16 BF16 bits of ``bf16(v)``."""
+    return int(np.array([bf16(v)], dtype=np.float32).view(np.uint32)[0] >> 16)
+
+
+def dx(x, w, grad_proj, grad_r, r, K: int, addend=None, mode: str = "tf32"):
+    """dX in FP64 for the rows and columns given.
+
+    x [rows, cols] FP32, w [24, cols] FP32 (the same columns), grad_proj
+    [rows, 32] FP32 (columns 24..31 are never read), grad_r and r [rows],
+    addend [rows, cols] as BF16 bits (uint16) or None; K is the full row
+    width used in grad_r / (r K).
+    """
+    lib = _load()
+    x, xp = _f32(x)
+    rows, cols = x.shape
+    w, wp = _f32(w)
+    gp, gpp = _f32(grad_proj)
+    gr, grp = _f32(grad_r)
+    rr, rp = _f32(r)
+    assert w.shape == (24, cols) and gp.shape == (rows, 32)
+    assert gr.shape == (rows,) and rr.shape == (rows,)
+    ap = None
+    if addend is not None:
+        addend = np.ascontiguousarray(addend, dtype=np.uint16)
+        assert addend.shape == (rows, cols)
+        ap = addend.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16))
+    out = np.empty((rows, cols), dtype=np.float64)
+    rc = lib.oracle_dx(_MODES[mode], rows, cols, int(K), xp, wp, gpp, grp, rp, ap,
+                       out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError("oracle_dx rejected its arguments")
+    return out
+
+
+def dw(x, grad_proj, mode: str = "tf32"):
+    """dW [24, cols] in FP64, summed over every row of x [rows, cols]."""
+    lib = _load()
+    x, xp = _f32(x)
+    rows, cols = x.shape
+    gp, gpp = _f32(grad_proj)
+    assert gp.shape == (rows, 32)
+    out = np.empty((24, cols), dtype=np.float64)
+    rc = lib.oracle_dw(_MODES[mode], rows, cols, xp, gpp,
+                       out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError("oracle_dw rejected its arguments")
+    return out
+
+
+def backward(x, w, grad_proj, grad_r, r, addend=None, mode: str = "tf32"):
+    """(dX, dW) in FP64 over a whole [T, K] problem."""
+    K = np.shape(x)[1]
+    return (dx(x, w, grad_proj, grad_r, r, K, addend=addend, mode=mode),
+            dw(x, grad_proj, mode=mode))

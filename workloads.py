@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs for the DSv4.1 mHC projection/RMS backward.
+
+This module only draws inputs; it holds none of the backward's arithmetic.
+Both the GPU path (through the C-ABI) and the CPU oracle consume what it makes.
+
+Shapes and distributions (the stage's supported training profile is 4 streams
+x hidden 5120 x 4096 tokens, "DSv4.1 mHC projection/RMS backward" page,
+introduction; the other sizes widen that profile):
+
+  X          FP32 [T, K], K = streams * hidden, N(0, 1)
+  W          FP32 [24, K], N(0, 0.02)  (0.02 is the standard deviation)
+  grad_proj  FP32 [T, 32], columns 0..23 N(0, 0.01); columns 24..31 hold
+             garbage (NaN in even columns, 1e30 in odd ones): the page says
+             they are ignored even if nonzero
+  grad_r     FP32 [T], N(0, 0.01)
+  r          FP32 [T], sqrt(mean(X^2, row) + 1e-6) computed in FP64 (the
+             positive forward RMS the page asks for)
+  addend     BF16 [T, K], N(0, 0.01) (the fused stream gradient,
+             prime-kernels pull request 15), only where a workload has one
+  rescale    where a workload asks for it, each X row is multiplied by
+             10^U(-2, 2) before r is computed, which stresses grad_r / (r K)
+
+Random numbers come from torch generators seeded per workload; a generator on
+the GPU draws different numbers from one on the CPU, so a test draws on one
+device and copies to the other.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+PROJ_COLS = 24
+PROJ_STRIDE = 32
+SEED_BASE = 20261202
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    streams: int
+    hidden: int
+    seed: int
+    addend: bool = False
+    rescale_rows: bool = False
+
+    @property
+    def K(self) -> int:
+        return self.streams * self.hidden
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("tiny", 512, 4, 512, SEED_BASE + 0),
+        Workload("train", 4096, 4, 5120, SEED_BASE + 1),
+        Workload("long", 16384, 4, 5120, SEED_BASE + 2),
+        Workload("addend", 16384, 4, 5120, SEED_BASE + 3, addend=True),
+        Workload("large", 65536, 4, 5120, SEED_BASE + 4, rescale_rows=True),
+        Workload("ragged", 4095, 4, 5120, SEED_BASE + 14, rescale_rows=True),
+    )
+}
+
+
+def custom(T: int, streams: int = 4, hidden: int = 512, seed: int = 1,
+           addend: bool = False, rescale_rows: bool = False) -> Workload:
+    """A workload of any shape, drawn from the same distributions."""
+    return Workload(f"T{T}_s{streams}_h{hidden}", T, streams, hidden, seed,
+                    addend, rescale_rows)
+
+
+def garbage_tail(T: int, device="cpu") -> torch.Tensor:
+    """[T, 8] FP32 garbage for the ignored grad_proj columns 24..31."""
+    tail = torch.empty(T, PROJ_STRIDE - PROJ_COLS, dtype=torch.float32, device=device)
+    tail[:, 0::2] = float("nan")
+    tail[:, 1::2] = 1e30
+    return tail
+
+
+def make(w: Workload, device="cpu") -> dict:
+    """Draw every input of workload ``w`` on ``device`` (torch tensors)."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    T, K = w.T, w.K
+    x = torch.randn(T, K, generator=g, device=dev, dtype=torch.float32)
+    if w.rescale_rows:
+        expo = torch.rand(T, 1, generator=g, device=dev, dtype=torch.float64) * 4.0 - 2.0
+        x.mul_(torch.pow(10.0, expo).to(torch.float32))
+    wt = torch.randn(PROJ_COLS, K, generator=g, device=dev, dtype=torch.float32) * 0.02
+    gp = torch.empty(T, PROJ_STRIDE, device=dev, dtype=torch.float32)
+    gp[:, :PROJ_COLS] = torch.randn(T, PROJ_COLS, generator=g, device=dev,
+                                    dtype=torch.float32) * 0.01
+    gp[:, PROJ_COLS:] = garbage_tail(T, dev)
+    grad_r = torch.randn(T, generator=g, device=dev, dtype=torch.float32) * 0.01
+    r = forward_rms(x)
+    out = dict(x=x, w=wt, grad_proj=gp, grad_r=grad_r, r=r, addend=None)
+    if w.addend:
+        a = torch.randn(T, K, generator=g, device=dev, dtype=torch.float32) * 0.01
+        out["addend"] = a.to(torch.bfloat16)
+    return out
+
+
+def forward_rms(x: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+    """The forward's positive RMS per row, in FP64, stored as FP32."""
+    rows = []
+    step = 1024
+    for i in range(0, x.shape[0], step):
+        xx = x[i:i + step].to(torch.float64)
+        rows.append(torch.sqrt((xx * xx).mean(dim=1) + eps).to(torch.float32))
+    if not rows:
+        return torch.empty(0, dtype=torch.float32, device=x.device)
+    return torch.cat(rows)
+
+
+def bf16_bits(t: torch.Tensor) -> torch.Tensor:
+    """Reinterpret a BF16 tensor as its uint16 bit patterns (int16 storage)."""
+    return t.view(torch.int16)
