@@ -1,0 +1,256 @@
+"""Benchmark of the DSv4.1 mHC projection/RMS backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
+
+One step is one call of mhcpb_execute (kernel 1 + kernel 2) on the synthetic
+workload, with every input already resident in HBM.  Prints ONE JSON line:
+microseconds per call, achieved GB/s of algorithmic bytes (value), the
+roofline of the dominant kernel (kernel 1, timed per launch with HIP events
+recorded by the library on the launch stream) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+Algorithmic bytes per call (T tokens, K columns, S splits):
+    X T*K*4 + dX T*K*2 [+ addend T*K*2] + W 24*K*4 + P 24*T*4 + grad_r, r 2*T*4
+    + partial dW slabs written and read 2*S*24*K*4 + dW 24*K*4
+Kernel 1 moves everything but the slab reads and the dW write.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBPS = 8000.0
+METRIC = "µs/call and achieved HBM GB/s (% of peak) at T=4096, K=4×5120"
+KERNEL_SOURCE = os.path.join(ROOT, "rms_backward_amd", "csrc", "mhcpb_kernels.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "projection_train_counters.json")
+
+
+def algorithmic_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
+    """(whole call, kernel 1) algorithmic bytes."""
+    big = T * K * 4 + T * K * 2 + (T * K * 2 if addend else 0)
+    small = 24 * K * 4 + 24 * T * 4 + 2 * T * 4
+    slabs = S * 24 * K * 4
+    k1 = big + small + slabs
+    call = k1 + slabs + 24 * K * 4
+    return call, k1
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per kernel-1 launch from the committed counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        h = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return h.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def destroy(self, h: int):
+        self.lib.hipEventDestroy(h)
+
+
+def cpu_baseline(inp, rows: int, T: int, K: int, S: int, addend: bool):
+    """Time the FP64 oracle (as it is, one thread) on the first `rows` rows."""
+    import numpy as np
+
+    import oracle
+    from tests import gpu_harness as gh
+
+    rows = min(rows, T)
+    h = gh.host_rows(inp, list(range(rows)))
+    t0 = time.perf_counter()
+    oracle.dx(h["x"], h["w"], h["grad_proj"], h["grad_r"], h["r"], K, addend=h["addend"],
+              mode="tf32")
+    oracle.dw(h["x"], h["grad_proj"], mode="tf32")
+    dt = time.perf_counter() - t0
+    call_bytes, _ = algorithmic_bytes(T, K, S, addend)
+    frac = rows / T
+    us_per_call = dt / frac * 1e6
+    del np
+    return {
+        "value": round(call_bytes * frac / dt / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {rows} of {T} rows, all {K} columns: dX rows and their dW "
+                   f"contribution, TF32-mode FP64 oracle, one thread; {dt:.2f} s"),
+        "us_per_call_extrapolated": round(us_per_call, 1),
+    }
+
+
+def run_copy_calibration(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="train")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="rows of the workload the CPU oracle baseline times")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES bytes (counter scaling)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this stage is measured on one GPU only; runs on more than one "
+              "GPU are not part of this build (--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_calibration:
+        run_copy_calibration(args.copy_calibration, max(1, args.steps))
+        return 0
+
+    import workloads
+    from rms_backward_amd import mhcpb_execute_with_events, mhcpb_plan_split_count
+    from rms_backward_amd.wrapper import Plan
+    from tests import gpu_harness as gh
+
+    wl = workloads.WORKLOADS[args.workload]
+    T, K = wl.T, wl.K
+    print(f"bench: workload {wl.name} T={T} K={K}", file=sys.stderr, flush=True)
+    inp = workloads.make(wl, "cuda")
+    plan = Plan(T, wl.streams, wl.hidden)
+    S = mhcpb_plan_split_count(plan.handle)
+    dx, dw, ws = gh.alloc_outputs(T, K, plan, "cuda", poison=True)
+    call = lambda: plan.execute(inp["x"], inp["w"], inp["grad_proj"], inp["grad_r"], inp["r"],
+                                dx, dw, ws, inp.get("addend"))
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` calls
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us_per_call = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    # per-kernel durations: the same calls, with HIP events the library records
+    # on the launch stream before kernel 1, between the kernels and after kernel 2
+    hev = HipEvents()
+    n = args.steps
+    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b, c in evs:
+        mhcpb_execute_with_events(plan.handle, inp["x"], inp["w"], inp["grad_proj"],
+                                  inp["grad_r"], inp["r"], dx, dw, inp.get("addend"), ws,
+                                  ws.numel(), stream.cuda_stream, a, b, c)
+    torch.cuda.synchronize()
+    k1_ms = [hev.elapsed_ms(a, b) for a, b, _ in evs]
+    k2_ms = [hev.elapsed_ms(b, c) for _, b, c in evs]
+    for trio in evs:
+        for e in trio:
+            hev.destroy(e)
+    k1_us = sum(k1_ms) / n * 1e3
+    k2_us = sum(k2_ms) / n * 1e3
+
+    call_bytes, k1_bytes = algorithmic_bytes(T, K, S, wl.addend)
+    gbps = call_bytes / (us_per_call * 1e-6) / 1e9
+    k1_gbps = k1_bytes / (k1_us * 1e-6) / 1e9
+    traffic = measured_traffic(wl.name)
+    out = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_call / 1e3, 6),
+        "us_per_call": round(us_per_call, 2),
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "tf32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name}: T={T} tokens, {wl.streams} streams x hidden "
+                         f"{wl.hidden} (K={K}); X/W/grad_proj/grad_r/r FP32, dX BF16, "
+                         f"dW FP32" + (", BF16 addend" if wl.addend else "")),
+            "T": T, "K": K, "splits": S,
+            "bytes_per_call": call_bytes,
+            "k1_us": round(k1_us, 2), "k2_us": round(k2_us, 2),
+            "timed_wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(k1_gbps, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "projection (kernel 1)",
+            "bytes_per_launch": k1_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, T, K, S, wl.addend)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,139 @@
+/*
+ * mhcpb.h -- C-ABI of the DSv4.1 mHC projection/RMS backward for MI355X
+ * (gfx950).
+ *
+ * The operation ("DSv4.1 mHC projection/RMS backward", cuDNN Frontend page,
+ * introduction): with P = grad_proj[:, :24],
+ *
+ *     dX = P W + grad_r / (r K) * X        stored as BF16
+ *     dW = P^T X                           stored as FP32
+ *
+ * over X of shape [T, K], K = streams * hidden.  Both matrix products round
+ * their operands to TF32 (round to nearest even of the FP32 fraction at 10
+ * bits) and accumulate in FP32; the RMS term is FP32 arithmetic on the raw x.
+ * dW is reduced from per-slab partial sums in a fixed order without atomics,
+ * so its bits depend only on (T, K) and this library, never on the CU count,
+ * the launch timing or the run.  Outputs are overwritten, not accumulated
+ * (same page, introduction).
+ *
+ * Tensor contract (same page, "Requirements and tensor contract"): compact
+ * row-major tensors, columns 24..31 of grad_proj are never read, r holds the
+ * positive forward RMS values, every operand, output and the workspace are
+ * disjoint and 16-byte aligned.  Anything else is rejected; nothing is
+ * converted or repacked.
+ *
+ * All device pointers are plain HIP device addresses owned by the caller.
+ * The library never allocates, frees or synchronizes device memory; a plan
+ * holds host metadata only ("Prepared class API" section: compile() does no
+ * tensor work, execute() allocates no tensor storage and enqueues exactly two
+ * kernels).  Every function returns a status and never throws; on any error
+ * no kernel is launched and no output is written.
+ */
+#ifndef MHCPB_H
+#define MHCPB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque plan: host memory only, immutable after creation. */
+typedef struct mhcpb_plan_s *mhcpb_plan_t;
+
+typedef enum mhcpb_status {
+    MHCPB_SUCCESS = 0,
+    MHCPB_ERROR_INVALID_ARGUMENT = 1, /* NULL plan or pointer, T < 1          */
+    MHCPB_ERROR_UNSUPPORTED = 2,      /* streams != 4, hidden odd or < 2,
+                                         sizes beyond the supported range     */
+    MHCPB_ERROR_MISALIGNED = 3,       /* a pointer not 16-byte aligned        */
+    MHCPB_ERROR_OVERLAP = 4,          /* two byte ranges intersect            */
+    MHCPB_ERROR_WORKSPACE = 5,        /* workspace smaller than required      */
+    MHCPB_ERROR_LAUNCH = 6            /* the HIP runtime refused a launch     */
+} mhcpb_status_t;
+
+/*
+ * Create a plan for X of shape [T, streams * hidden].
+ *   T       tokens, 1 <= T <= 2^31 - 1
+ *   streams residual streams; must be 4 (the page's supported profile)
+ *   hidden  hidden size per stream; even, 2 <= hidden <= 2^20, so that every
+ *           BF16 row of dX is a multiple of 16 bytes
+ * Host work only: the split schedule, the grid and the workspace size.  The
+ * split count S depends on T alone (S = min(32, ceil(T / 512))), which is
+ * what makes dW bitwise reproducible across devices with different CU counts.
+ * On success *plan receives a new plan; on error *plan is set to NULL.
+ */
+mhcpb_status_t mhcpb_plan_create(mhcpb_plan_t *plan, int64_t T, int32_t streams,
+                                 int32_t hidden);
+
+/* Free a plan (host memory).  NULL is accepted and ignored. */
+mhcpb_status_t mhcpb_plan_destroy(mhcpb_plan_t plan);
+
+/*
+ * Bytes of device workspace execute() needs: S * 24 * K * 4, one FP32 [24, K]
+ * partial dW slab per split ("Prepared class API": 15,728,640 bytes at T =
+ * 4096, 4 streams, hidden 5120, i.e. S = 8).  Contents are undefined on entry
+ * and on exit; the workspace is caller-owned.
+ */
+mhcpb_status_t mhcpb_workspace_bytes(mhcpb_plan_t plan, size_t *bytes);
+
+/* The split count S(T) of the plan (for schedule inspection). */
+mhcpb_status_t mhcpb_plan_split_count(mhcpb_plan_t plan, int32_t *splits);
+
+/*
+ * Enqueue the stage on `stream` (0 = the null stream): kernel 1 streams X
+ * once, writes dX and one partial dW slab per split into the workspace;
+ * kernel 2 sums the slabs in ascending split order into dW.
+ *
+ *   x              [T, K]  FP32 input
+ *   w              [24, K] FP32 projection weight
+ *   grad_proj      [T, 32] FP32; columns 24..31 are never read (NaN is fine)
+ *   grad_r         [T]     FP32 gradient of the RMS value
+ *   r              [T]     FP32 forward RMS, positive (not checked on device;
+ *                          other values follow IEEE arithmetic)
+ *   dx             [T, K]  BF16 bit patterns, overwritten
+ *   dw             [24, K] FP32, overwritten
+ *   grad_x_addend  [T, K]  BF16 or NULL.  When given it is added to the FP32
+ *                          dX value before the single rounding to BF16 (the
+ *                          fused stream gradient of prime-kernels pull
+ *                          request 15, "fused mHC stream gradient" item)
+ *   workspace      >= mhcpb_workspace_bytes(plan) bytes of device memory
+ *   workspace_size the size of that buffer in bytes
+ *
+ * Every pointer must be 16-byte aligned and every byte range disjoint from
+ * the others.  The call only validates and launches: it returns before the
+ * kernels finish, and the caller keeps every buffer alive until the stream
+ * work completes.  Concurrent calls are safe when they use separate outputs
+ * and workspaces ("Prepared class API").  Because the call is launch-only it
+ * can be recorded into a HIP graph.
+ */
+mhcpb_status_t mhcpb_execute(mhcpb_plan_t plan, const float *x, const float *w,
+                             const float *grad_proj, const float *grad_r,
+                             const float *r, uint16_t *dx, float *dw,
+                             const uint16_t *grad_x_addend, void *workspace,
+                             size_t workspace_size, hipStream_t stream);
+
+/*
+ * Same as mhcpb_execute, and records `before_k1`, `after_k1` and `after_k2`
+ * on `stream` around the two kernels (any of them may be NULL), so a caller
+ * can time each kernel with hipEventElapsedTime.  The events are created and
+ * owned by the caller.
+ */
+mhcpb_status_t mhcpb_execute_with_events(
+    mhcpb_plan_t plan, const float *x, const float *w, const float *grad_proj,
+    const float *grad_r, const float *r, uint16_t *dx, float *dw,
+    const uint16_t *grad_x_addend, void *workspace, size_t workspace_size,
+    hipStream_t stream, hipEvent_t before_k1, hipEvent_t after_k1,
+    hipEvent_t after_k2);
+
+/* A static, human-readable name for a status code. */
+const char *mhcpb_status_string(mhcpb_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHCPB_H */

@@ -1,0 +1,143 @@
+"""MI355X (gfx950) DSv4.1 mHC projection/RMS backward.
+
+A thin ctypes binding over the C-ABI of ``libmhcpb.so`` (declared in
+``include/mhcpb.h``), with the same function names.  Every step of the stage
+runs in the library's HIP kernels; this module only marshals arguments.  If the
+library has not been built, importing this package raises: there is no other
+implementation to fall back on.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+try:
+    # When PyTorch is present, load its HIP runtime first so that this
+    # library binds to the same libamdhip64 instance as torch's allocations.
+    import torch  # noqa: F401
+except ImportError:  # the library itself does not need torch
+    torch = None
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmhcpb.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m rms_backward_amd.build` "
+        "(hipcc, gfx950) before using rms_backward_amd")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MHCPB_SUCCESS = 0
+MHCPB_ERROR_INVALID_ARGUMENT = 1
+MHCPB_ERROR_UNSUPPORTED = 2
+MHCPB_ERROR_MISALIGNED = 3
+MHCPB_ERROR_OVERLAP = 4
+MHCPB_ERROR_WORKSPACE = 5
+MHCPB_ERROR_LAUNCH = 6
+
+EXPORTED = (
+    "mhcpb_plan_create", "mhcpb_plan_destroy", "mhcpb_workspace_bytes",
+    "mhcpb_plan_split_count", "mhcpb_execute", "mhcpb_execute_with_events",
+    "mhcpb_status_string",
+)
+
+_vp = ctypes.c_void_p
+_lib.mhcpb_plan_create.argtypes = [ctypes.POINTER(_vp), ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_int32]
+_lib.mhcpb_plan_create.restype = ctypes.c_int
+_lib.mhcpb_plan_destroy.argtypes = [_vp]
+_lib.mhcpb_plan_destroy.restype = ctypes.c_int
+_lib.mhcpb_workspace_bytes.argtypes = [_vp, ctypes.POINTER(ctypes.c_size_t)]
+_lib.mhcpb_workspace_bytes.restype = ctypes.c_int
+_lib.mhcpb_plan_split_count.argtypes = [_vp, ctypes.POINTER(ctypes.c_int32)]
+_lib.mhcpb_plan_split_count.restype = ctypes.c_int
+_EXEC_ARGS = [_vp] * 10 + [ctypes.c_size_t, _vp]
+_lib.mhcpb_execute.argtypes = _EXEC_ARGS
+_lib.mhcpb_execute.restype = ctypes.c_int
+_lib.mhcpb_execute_with_events.argtypes = _EXEC_ARGS + [_vp, _vp, _vp]
+_lib.mhcpb_execute_with_events.restype = ctypes.c_int
+_lib.mhcpb_status_string.argtypes = [ctypes.c_int]
+_lib.mhcpb_status_string.restype = ctypes.c_char_p
+
+
+class MhcpbError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mhcpb_status_string(status)} (status {status})")
+
+
+def mhcpb_status_string(status: int) -> str:
+    return _lib.mhcpb_status_string(int(status)).decode()
+
+
+def _ptr(t) -> int | None:
+    """Device address of a tensor (torch) or an int address; None stays NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def mhcpb_plan_create(T: int, streams: int, hidden: int) -> int:
+    """Create a plan; returns its opaque handle.  Raises MhcpbError on error."""
+    h = _vp()
+    st = _lib.mhcpb_plan_create(ctypes.byref(h), int(T), int(streams), int(hidden))
+    if st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_plan_create")
+    return h.value
+
+
+def mhcpb_plan_create_status(T: int, streams: int, hidden: int) -> tuple[int, int | None]:
+    """(status, handle-or-None) without raising, for argument-check tests."""
+    h = _vp()
+    st = _lib.mhcpb_plan_create(ctypes.byref(h), int(T), int(streams), int(hidden))
+    return st, h.value
+
+
+def mhcpb_plan_destroy(plan: int | None) -> None:
+    _lib.mhcpb_plan_destroy(plan)
+
+
+def mhcpb_workspace_bytes(plan: int) -> int:
+    n = ctypes.c_size_t()
+    st = _lib.mhcpb_workspace_bytes(plan, ctypes.byref(n))
+    if st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_workspace_bytes")
+    return n.value
+
+
+def mhcpb_plan_split_count(plan: int) -> int:
+    n = ctypes.c_int32()
+    st = _lib.mhcpb_plan_split_count(plan, ctypes.byref(n))
+    if st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_plan_split_count")
+    return n.value
+
+
+def mhcpb_execute(plan, x, w, grad_proj, grad_r, r, dx, dw, grad_x_addend, workspace,
+                  workspace_size: int, stream: int = 0, check: bool = True) -> int:
+    """Enqueue the stage.  Tensors are passed by device address (torch tensors
+    or ints); ``stream`` is a raw hipStream_t (0 = null stream).  Returns the
+    status; raises MhcpbError on a non-zero status when ``check`` is set."""
+    st = _lib.mhcpb_execute(plan, _ptr(x), _ptr(w), _ptr(grad_proj), _ptr(grad_r), _ptr(r),
+                            _ptr(dx), _ptr(dw), _ptr(grad_x_addend), _ptr(workspace),
+                            int(workspace_size), stream)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_execute")
+    return st
+
+
+def mhcpb_execute_with_events(plan, x, w, grad_proj, grad_r, r, dx, dw, grad_x_addend,
+                              workspace, workspace_size: int, stream: int,
+                              before_k1: int | None, after_k1: int | None,
+                              after_k2: int | None, check: bool = True) -> int:
+    """mhcpb_execute that also records three caller-owned hipEvent_t handles."""
+    st = _lib.mhcpb_execute_with_events(
+        plan, _ptr(x), _ptr(w), _ptr(grad_proj), _ptr(grad_r), _ptr(r), _ptr(dx), _ptr(dw),
+        _ptr(grad_x_addend), _ptr(workspace), int(workspace_size), stream,
+        before_k1, after_k1, after_k2)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_execute_with_events")
+    return st

@@ -1,0 +1,55 @@
+// Internal declarations shared by the plan/validation code and the kernels.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace mhcpb {
+
+constexpr int kProjCols = 24;    // columns of grad_proj that take part
+constexpr int kProjStride = 32;  // row length of grad_proj (8 ignored columns)
+constexpr int kMaxSplits = 32;
+constexpr int64_t kRowsPerSplit = 512;
+
+// Split count as a function of T only: one partial dW slab per 512 tokens,
+// at most 32.  At T = 4096 this gives the 8 slabs whose FP32 [24, K] partials
+// make the 15,728,640-byte workspace of the page's supported profile.
+inline int32_t split_count(int64_t T) {
+    int64_t s = (T + kRowsPerSplit - 1) / kRowsPerSplit;
+    return static_cast<int32_t>(s > kMaxSplits ? kMaxSplits : s);
+}
+
+struct Plan {
+    int64_t T;
+    int32_t streams;
+    int32_t hidden;
+    int64_t K;
+    int32_t S;        // splits (partial dW slabs)
+    int64_t L;        // rows per slab, ceil(T / S); the last slab may be shorter
+    size_t ws_bytes;  // S * 24 * K * 4
+};
+
+struct Args {
+    const float *x;
+    const float *w;
+    const float *grad_proj;
+    const float *grad_r;
+    const float *r;
+    uint16_t *dx;
+    float *dw;
+    const uint16_t *addend;  // may be null
+    float *ws;
+};
+
+// Kernel 1: one pass over X; writes dX and the S partial dW slabs.
+hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream);
+// Kernel 2: dW = sum of the S slabs in ascending order.
+hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream);
+
+}  // namespace mhcpb
+
+struct mhcpb_plan_s {
+    mhcpb::Plan plan;
+};

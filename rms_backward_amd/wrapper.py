@@ -1,0 +1,61 @@
+"""Allocating convenience call over the C-ABI, for PyTorch callers.
+
+Mirrors the page's allocating wrapper ("DSv4.1 mHC projection/RMS backward",
+"Allocating wrapper" section): it allocates dX, dW and the workspace with torch
+on the tensors' device, enqueues the stage on the current (or given) stream and
+returns (dx, dw).  The caller orders streams and keeps tensors alive.  All
+arithmetic happens in the library's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (mhcpb_execute, mhcpb_plan_create, mhcpb_plan_destroy,
+               mhcpb_workspace_bytes)
+
+PROJ_COLS = 24
+
+
+class Plan:
+    """Owns a plan handle for one (T, streams, hidden)."""
+
+    def __init__(self, T: int, streams: int, hidden: int):
+        self.T, self.streams, self.hidden = int(T), int(streams), int(hidden)
+        self.K = self.streams * self.hidden
+        self.handle = mhcpb_plan_create(self.T, self.streams, self.hidden)
+        self.workspace_bytes = mhcpb_workspace_bytes(self.handle)
+
+    def close(self):
+        if self.handle:
+            mhcpb_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc_workspace(self, device) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device)
+
+    def execute(self, x, w, grad_proj, grad_r, r, dx, dw, workspace,
+                grad_x_addend=None, stream=None):
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        return mhcpb_execute(self.handle, x, w, grad_proj, grad_r, r, dx, dw,
+                             grad_x_addend, workspace, workspace.numel(), s.cuda_stream)
+
+
+def mhc_projection_backward(x, w, grad_proj, grad_r, r, grad_x_addend=None, stream=None):
+    """Allocate outputs and workspace, run the stage, return (dx, dw).
+
+    dx is BF16 [T, K], dw is FP32 [24, K].
+    """
+    T, K = x.shape
+    assert K % 4 == 0
+    plan = Plan(T, 4, K // 4)
+    dx = torch.empty(T, K, dtype=torch.bfloat16, device=x.device)
+    dw = torch.empty(PROJ_COLS, K, dtype=torch.float32, device=x.device)
+    ws = plan.alloc_workspace(x.device)
+    plan.execute(x, w, grad_proj, grad_r, r, dx, dw, ws, grad_x_addend, stream)
+    return dx, dw

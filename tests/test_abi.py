@@ -1,0 +1,191 @@
+"""Host-side checks of the C-ABI library (no kernel is ever launched here).
+
+* the library loads and exports every function include/mhcpb.h declares;
+* plan creation accepts the supported domain and rejects the rest;
+* the workspace at the page's supported profile is the printed 15,728,640
+  bytes ("DSv4.1 mHC projection/RMS backward", "Prepared class API");
+* the split schedule depends on T only;
+* execute() rejects NULL, misaligned and overlapping pointers and a short
+  workspace before touching the GPU ("Requirements and tensor contract").
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rms_backward_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "mhcpb.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhcpb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert "mhcpb_execute" in names and "mhcpb_plan_create" in names
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(m.EXPORTED)
+
+
+def test_workspace_at_supported_profile_matches_page():
+    line = [l for l in open(os.path.join(ROOT, "tests", "golden", "workspace_profile.txt"))
+            if l.strip() and not l.startswith("#")][0]
+    T, streams, hidden, ws = (int(v) for v in line.split())
+    plan = m.mhcpb_plan_create(T, streams, hidden)
+    try:
+        assert m.mhcpb_workspace_bytes(plan) == ws == 15728640
+        assert m.mhcpb_plan_split_count(plan) == 8
+    finally:
+        m.mhcpb_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("T,expect", [(1, 1), (511, 1), (512, 1), (513, 2), (4095, 8),
+                                      (4096, 8), (4097, 9), (16383, 32), (16384, 32),
+                                      (65536, 32), (2**31 - 1, 32)])
+def test_split_count_depends_on_T_only(T, expect):
+    for hidden in (2, 512, 5120):
+        plan = m.mhcpb_plan_create(T, 4, hidden)
+        try:
+            assert m.mhcpb_plan_split_count(plan) == expect
+            assert m.mhcpb_workspace_bytes(plan) == expect * 24 * 4 * hidden * 4
+        finally:
+            m.mhcpb_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("T,streams,hidden,status", [
+    (0, 4, 512, m.MHCPB_ERROR_INVALID_ARGUMENT),
+    (-5, 4, 512, m.MHCPB_ERROR_INVALID_ARGUMENT),
+    (2**31, 4, 512, m.MHCPB_ERROR_UNSUPPORTED),
+    (16, 3, 512, m.MHCPB_ERROR_UNSUPPORTED),
+    (16, 8, 512, m.MHCPB_ERROR_UNSUPPORTED),
+    (16, 4, 511, m.MHCPB_ERROR_UNSUPPORTED),
+    (16, 4, 0, m.MHCPB_ERROR_UNSUPPORTED),
+    (16, 4, 2**20 + 2, m.MHCPB_ERROR_UNSUPPORTED),
+])
+def test_plan_create_rejects(T, streams, hidden, status):
+    st, h = m.mhcpb_plan_create_status(T, streams, hidden)
+    assert st == status
+    assert h is None
+
+
+def test_status_strings():
+    for st in range(7):
+        assert m.mhcpb_status_string(st)
+    assert "align" in m.mhcpb_status_string(m.MHCPB_ERROR_MISALIGNED)
+
+
+def _no_gpu_visible():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+# The calls below hand the library fake device addresses that it only checks.
+# Each one must fail validation before any launch; as a second guard they are
+# never run where a GPU is visible.
+fake_addresses = pytest.mark.skipif(not _no_gpu_visible(),
+                                    reason="fake device addresses are used only without a GPU")
+
+
+class _FakeBuffers:
+    """Disjoint, aligned fake device addresses: validation never dereferences
+    them, and none of these calls reaches a launch."""
+
+    def __init__(self, T, hidden):
+        K = 4 * hidden
+        sizes = dict(x=T * K * 4, w=24 * K * 4, grad_proj=T * 128, grad_r=T * 4, r=T * 4,
+                     dx=T * K * 2, dw=24 * K * 4, addend=T * K * 2,
+                     ws=m.mhcpb_workspace_bytes(m.mhcpb_plan_create(T, 4, hidden)) + 256)
+        base = 1 << 40
+        self.addr = {}
+        for k, n in sizes.items():
+            self.addr[k] = base
+            base += (n + 4095) // 4096 * 4096 + 4096
+        self.ws_size = sizes["ws"]
+        self.ws_needed = sizes["ws"] - 256
+
+    def args(self, **over):
+        a = dict(self.addr)
+        a.update(over)
+        return a
+
+
+def _exec(plan, a, ws_size):
+    return m.mhcpb_execute(plan, a["x"], a["w"], a["grad_proj"], a["grad_r"], a["r"],
+                           a["dx"], a["dw"], a.get("addend"), a["ws"], ws_size, 0,
+                           check=False)
+
+
+@pytest.mark.parametrize("field", ["x", "w", "grad_proj", "grad_r", "r", "dx", "dw", "ws",
+                                   "addend"])
+@fake_addresses
+def test_execute_rejects_misaligned(field):
+    plan = m.mhcpb_plan_create(64, 4, 64)
+    fb = _FakeBuffers(64, 64)
+    try:
+        for off in (1, 4, 8):
+            a = fb.args(**{field: fb.addr[field] + off})
+            assert _exec(plan, a, fb.ws_size) == m.MHCPB_ERROR_MISALIGNED
+    finally:
+        m.mhcpb_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("field", ["x", "w", "grad_proj", "grad_r", "r", "dx", "dw", "ws"])
+@fake_addresses
+def test_execute_rejects_null(field):
+    plan = m.mhcpb_plan_create(64, 4, 64)
+    fb = _FakeBuffers(64, 64)
+    try:
+        a = fb.args(**{field: None})
+        assert _exec(plan, a, fb.ws_size) == m.MHCPB_ERROR_INVALID_ARGUMENT
+        assert _exec(None, fb.args(), fb.ws_size) == m.MHCPB_ERROR_INVALID_ARGUMENT
+    finally:
+        m.mhcpb_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("a,b", [("x", "dx"), ("dx", "dw"), ("ws", "dw"), ("addend", "dx"),
+                                 ("r", "grad_r"), ("w", "grad_proj"), ("x", "addend")])
+@fake_addresses
+def test_execute_rejects_overlap(a, b):
+    plan = m.mhcpb_plan_create(64, 4, 64)
+    fb = _FakeBuffers(64, 64)
+    try:
+        # b starts 16 bytes before the end of a
+        K = 256
+        size = dict(x=64 * K * 4, dx=64 * K * 2, ws=fb.ws_needed, addend=64 * K * 2,
+                    r=64 * 4, w=24 * K * 4)[a]
+        args = fb.args(**{b: fb.addr[a] + size - 16})
+        assert _exec(plan, args, fb.ws_size) == m.MHCPB_ERROR_OVERLAP
+        args = fb.args(**{b: fb.addr[a]})
+        assert _exec(plan, args, fb.ws_size) == m.MHCPB_ERROR_OVERLAP
+    finally:
+        m.mhcpb_plan_destroy(plan)
+
+
+@fake_addresses
+def test_execute_rejects_short_workspace():
+    plan = m.mhcpb_plan_create(4096, 4, 5120)
+    fb = _FakeBuffers(4096, 5120)
+    try:
+        need = m.mhcpb_workspace_bytes(plan)
+        assert _exec(plan, fb.args(), need - 1) == m.MHCPB_ERROR_WORKSPACE
+        assert _exec(plan, fb.args(), 0) == m.MHCPB_ERROR_WORKSPACE
+    finally:
+        m.mhcpb_plan_destroy(plan)
+
+
+def test_null_plan_queries():
+    lib = ctypes.CDLL(m.LIB_PATH)
+    n = ctypes.c_size_t()
+    lib.mhcpb_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
+    assert lib.mhcpb_workspace_bytes(None, ctypes.byref(n)) == m.MHCPB_ERROR_INVALID_ARGUMENT
+    lib.mhcpb_plan_create.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_int32]
+    assert lib.mhcpb_plan_create(None, 16, 4, 64) == m.MHCPB_ERROR_INVALID_ARGUMENT
+    assert m.mhcpb_plan_destroy(None) is None
