@@ -180,8 +180,11 @@ struct ChunkLds {
 //      times TF32(P[j]), j = 16 jb + l%16: per MFMA, each lane group g holds
 //      two tokens x (x hi, x lo) x (P hi, P lo) = 8 exact partial products.
 // D is the depth of the per-wave LDS ring of X steps.
+// Minimum waves per SIMD the register allocation must allow.  With 4-wave
+// workgroups and a 3-deep ring the LDS (81 KB per workgroup) already limits a
+// CU to 2 workgroups, i.e. 2 waves per SIMD.
 #ifndef MHCPB_WAVES_PER_EU
-#define MHCPB_WAVES_PER_EU 3
+#define MHCPB_WAVES_PER_EU 2
 #endif
 
 template <int NW, int D, bool kAddend>

@@ -76,12 +76,17 @@ def sample_rows(T, L, rng, extra=24):
     return rows
 
 
-def sample_cols(K, rng, extra=24, tile=256):
-    """Edge columns, tile boundaries and random columns."""
+def sample_cols(K, rng, extra=24, tile=256, whole_first=0):
+    """Edge columns, tile boundaries, random columns, and optionally every
+    column of [0, whole_first), interleaved so that any prefix of the list
+    mixes the whole block with the scattered columns."""
+    head = list(range(min(whole_first, K)))
     cols = {0, 1, 2, 3, K - 4, K - 3, K - 2, K - 1}
     for b in (tile, 2 * tile, K // 2, K - tile):
         for d in (-4, -1, 0, 1, 4):
             if 0 <= b + d < K:
                 cols.add(b + d)
     cols.update(int(v) for v in rng.integers(0, K, size=extra))
-    return sorted(cols)
+    rest = sorted(c for c in cols if c >= len(head))
+    # keep a spread of columns (not only the head block) among the first ones
+    return [v for pair in zip(rest, head) for v in pair] + rest[len(head):] + head[len(rest):]
