@@ -45,6 +45,15 @@ constexpr int kRsrcWord3 = 0x00020000;
 // Offsets at or above this are outside every buffer range used here.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int64_t kMaxRecords = 0x7FFFFFF0;
+// Cache policy of the X stream (read once): non-temporal ("nt" on gfx950).
+#ifndef MHCPB_X_AUX
+#define MHCPB_X_AUX 2
+#endif
+// Cache policy of the dX stores (written once, read by a later stage):
+// non-temporal as well.
+#ifndef MHCPB_DX_AUX
+#define MHCPB_DX_AUX 2
+#endif
 
 // Two FP32 values to two BF16 (round to nearest even) packed low-first; one
 // v_cvt_pk_bf16_f32 on gfx950.
@@ -183,13 +192,14 @@ struct ChunkLds {
 // Minimum waves per SIMD the register allocation must allow.  With 4-wave
 // workgroups and a 3-deep ring the LDS (81 KB per workgroup) already limits a
 // CU to 2 workgroups, i.e. 2 waves per SIMD.
-#ifndef MHCPB_WAVES_PER_EU
-#define MHCPB_WAVES_PER_EU 2
-#endif
+// Minimum waves per SIMD the register allocation must allow: two 5-wave
+// workgroups per CU need 3 (at most 168 VGPRs); with 4-wave workgroups the
+// LDS already limits a CU to two workgroups, i.e. 2 waves per SIMD.
+constexpr int waves_per_eu(int nw) { return nw == 5 ? 3 : 2; }
 
 template <int NW, int D, bool kAddend>
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(MHCPB_WAVES_PER_EU))) void projection_kernel(
+__attribute__((amdgpu_waves_per_eu(waves_per_eu(NW)))) void projection_kernel(
     const float *__restrict__ x, const float *__restrict__ w,
     const float *__restrict__ grad_proj, const float *__restrict__ grad_r,
     const float *__restrict__ r, uint16_t *__restrict__ dx, float *__restrict__ ws,
@@ -321,7 +331,7 @@ __attribute__((amdgpu_waves_per_eu(MHCPB_WAVES_PER_EU))) void projection_kernel(
         for (int rr = 0; rr < 4; ++rr)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xrs, (MHCPB_LDS void *)(&xring[wave][stage][rr][0]), 16, xoffr[rr],
-                0, 0, 0);
+                0, 0, MHCPB_X_AUX);
     };
 
     // The dW operand rows j = 24..31 of both P buffers are zero padding.
@@ -454,7 +464,7 @@ __attribute__((amdgpu_waves_per_eu(MHCPB_WAVES_PER_EU))) void projection_kernel(
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[rr][0], packed[rr][1]}, drs,
-                                                      doffr[rr], 0, 0);
+                                                      doffr[rr], 0, MHCPB_DX_AUX);
         }
         stage_store(chunk[(ch + 1) & 1], c0 + kChunk);
         lds_barrier();
@@ -499,16 +509,6 @@ __global__ __launch_bounds__(256) void reduce_slabs(const float *__restrict__ ws
     reinterpret_cast<float4 *>(dw)[i] = a;
 }
 
-// Launch shape: 4 waves (256 columns) per workgroup and a 3-deep X ring.
-// These choices do not change any result bit (each column's dW is summed in
-// the same order whatever the workgroup width or ring depth).
-#ifndef MHCPB_NW
-#define MHCPB_NW 4
-#endif
-#ifndef MHCPB_DEPTH
-#define MHCPB_DEPTH 3
-#endif
-
 template <int NW, int D>
 hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream) {
     constexpr int cols = NW * 64;
@@ -525,8 +525,15 @@ hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream)
 
 }  // namespace
 
+// Launch shape, a performance choice only: each column's dW is summed in the
+// same order whatever the workgroup width, so every shape gives the same bits.
+// With 8 or fewer splits a 5-wave workgroup (320 columns) makes the grid one
+// full round of two workgroups per CU at K = 20480 on 256 CUs; with more
+// splits the grid is several rounds anyway and 4-wave workgroups stream
+// better.
 hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream) {
-    return launch_projection_t<MHCPB_NW, MHCPB_DEPTH>(p, a, stream);
+    if (p.S <= 8) return launch_projection_t<5, 3>(p, a, stream);
+    return launch_projection_t<4, 3>(p, a, stream);
 }
 
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream) {
