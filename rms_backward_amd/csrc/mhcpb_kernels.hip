@@ -14,13 +14,17 @@
 // significant bits; it splits exactly into a BF16 high part (its upper 16
 // bits) and a BF16 low part (the remaining 3 bits), so the four BF16 partial
 // products hi*hi, hi*lo, lo*hi, lo*lo are exact and their FP32 sum is the
-// TF32 product accumulated in FP32.  96 such products per dX element (24 j x
-// 4) fill exactly three 32-deep MFMAs; for dW the 48 (j, part) products of
-// the P side fill three 16-wide MFMA column blocks.
+// TF32 product accumulated in FP32.  Each MFMA k slot pairs one part of one
+// operand with one part of the other: for dX the W side is held in registers
+// as packed (hi, lo) pairs and the P side is staged in LDS with each part
+// repeated, 4 MFMAs per 16x16 output block (24 j padded to 32); for dW the X
+// side is split in registers and the P side is staged per part, 4 MFMAs per
+// column group.  No operand needs a per-step shuffle.
 //
 // X is streamed from HBM straight into LDS with buffer_load_dwordx4 ... lds,
 // a ring of D steps per wave, so prefetching costs no registers; rows past
-// the slab end fall outside the buffer range and arrive as zeros.
+// the slab end fall outside the buffer range and arrive as zeros.  The P rows
+// of each step arrive the same way a few steps ahead.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -44,7 +48,6 @@ constexpr int kWave = 64;
 constexpr int kRsrcWord3 = 0x00020000;
 // Offsets at or above this are outside every buffer range used here.
 constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int64_t kMaxRecords = 0x7FFFFFF0;
 // Cache policy of the X stream (read once): non-temporal ("nt" on gfx950).
 #ifndef MHCPB_X_AUX
 #define MHCPB_X_AUX 2
@@ -94,25 +97,14 @@ __device__ __forceinline__ uint32_t tf32_split_packed(float v) {
     return ((u & 0x7F800000u) == 0x7F800000u) ? quiet : finite;
 }
 
-// v_perm_b32 that stays where it is written: the W operands are rebuilt
-// inside the loop on purpose, and a plain builtin would be hoisted out of it
-// (keeping all expanded operands live and spilling).
-__device__ __forceinline__ uint32_t perm_in_place(uint32_t v, uint32_t sel) {
-    uint32_t r;
-    asm volatile("v_perm_b32 %0, %1, %1, %2" : "=v"(r) : "v"(v), "s"(sel));
-    return r;
+// Upper halves of two 32-bit words: (a >> 16) | (b & 0xFFFF0000).
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// [lo0 lo0 lo1 lo1 hi0 hi0 hi1 hi1] from (lo0 | hi0 << 16, lo1 | hi1 << 16).
-__device__ __forceinline__ u32x4 dup_halves(u32x2 p) {
-    return u32x4{perm_in_place(p.x, 0x01000100u), perm_in_place(p.y, 0x01000100u),
-                 perm_in_place(p.x, 0x03020302u), perm_in_place(p.y, 0x03020302u)};
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const int64_t n = bytes <= 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(n),
-                                             kRsrcWord3);
+// Buffer resource over [base, base + bytes) with bytes in [0, 2^31).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kRsrcWord3);
 }
 
 // LDS reads the compiler does not track.  X in LDS was written by LDS DMA,
@@ -133,6 +125,12 @@ __device__ __forceinline__ u32x4 lds_read_u128(uint32_t addr) {
     return v;
 }
 
+__device__ __forceinline__ float lds_read_f32(uint32_t addr) {
+    float v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
 __device__ __forceinline__ u32x2 lds_read_u64(uint32_t addr) {
     u32x2 v;
     asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr));
@@ -145,8 +143,12 @@ __device__ __forceinline__ void lds_write_u32(uint32_t addr, uint32_t v) {
     asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-__device__ __forceinline__ void lds_write_u64(uint32_t addr, u32x2 v) {
-    asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+__device__ __forceinline__ void lds_write_u128(uint32_t addr, u32x4 v) {
+    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ void lds_write_u16(uint32_t addr, uint32_t v) {
+    asm volatile("ds_write_b16 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -168,33 +170,54 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// P rows staged per chunk, and LDS strides (padded against bank conflicts).
-constexpr int kChunk = 32;
-constexpr int kStepsPerChunk = kChunk / 16;
-constexpr int kPsStride = 26;          // uint32 per row of packed (hi | lo << 16) P
-constexpr int kPtStride = kChunk + 4;  // uint32 per j row of transposed packed P
+// Rows per step (one MFMA row block) and the LDS layouts of P.
+constexpr int kStepRows = 16;
+constexpr int kJPad = 32;                 // j slots per part, 24..31 zero
+constexpr int kPaStride = 2 * kJPad + 4;  // uint32 per row of the dX P operand
+constexpr int kPbStride = kStepRows + 4;  // uint16 per (part, j) row of the dW P operand
 
-struct ChunkLds {
-    uint32_t ps[kChunk * kPsStride];  // [row][j]: hi | lo << 16
-    uint32_t pt[32 * kPtStride];  // [j][row]: hi | lo << 16; rows 24..31 stay zero
-    float c[kChunk];                  // grad_r / (r K)
+// The P of one step as it is stored in HBM, copied by LDS DMA: 16 rows of
+// grad_proj (32 floats each; the last 8 are never read from here), and one
+// grad_r and r entry per DMA lane (only the first 16 are used).
+struct RawStep {
+    f32x4 p[kStepRows * kProjStride / 4];
+    float gr[kWave];
+    float r[kWave];
+};
+
+// The P of one step in operand form (TF32 split into BF16 high and low parts):
+//  pa[row][part * 32 + j]: the part, duplicated in both halves of the word, as
+//      the dX product reads it (4 consecutive j per lane group);
+//  pb[part][j][row]: the part, as the dW product reads it (4 consecutive rows);
+//  c[row]: grad_r / (r K).
+// Entries with j >= 24 are zero and never written after the first clear.
+struct StepP {
+    uint32_t pa[kStepRows * kPaStride];
+    uint16_t pb[2 * kJPad * kPbStride];
+    float c[kStepRows];
 };
 
 // Kernel 1.  A workgroup of NW waves owns NW * 64 columns of one slab.  Per
 // step a wave handles 16 rows x 64 columns: lane l (c = l % 16, g = l / 16)
 // holds x[t0 + 4g + r][kw + 4c + i] for r, i in 0..3.
-//  dX: C_i[e] = dX[t0 + 4g + e][kw + 4c + i] = c_t x + sum over 96 slots of
-//      (P hi|lo of token t0 + l%16) x (W hi|lo of column kw + 4c + i).
-//  dW: acc[i][jb][e] = sum over tokens of TF32(x) of column kw + 4(4g+e) + i
-//      times TF32(P[j]), j = 16 jb + l%16: per MFMA, each lane group g holds
-//      two tokens x (x hi, x lo) x (P hi, P lo) = 8 exact partial products.
-// D is the depth of the per-wave LDS ring of X steps.
-// Minimum waves per SIMD the register allocation must allow.  With 4-wave
-// workgroups and a 3-deep ring the LDS (81 KB per workgroup) already limits a
-// CU to 2 workgroups, i.e. 2 waves per SIMD.
+//  dX: C_i[e] = dX[t0 + 4g + e][kw + 4c + i] = c_t x + the products of the P
+//      parts (token t0 + l%16) with the W parts (column kw + 4c + i): per
+//      MFMA (P part p, j block b) lane group g covers j = 16b + 4g .. +3 times
+//      (W hi, W lo); 4 MFMAs cover the 96 products of 24 j (8 padded).
+//  dW: acc[i][b][e] = sum over tokens of TF32(x) of column kw + 4(4g+e) + i
+//      times TF32(P[j]), j = 16 b + l%16: per MFMA (P part p), lane group g
+//      covers rows 4g .. 4g+3 times (x hi, x lo).
+//
+// Memory pipeline.  Each wave streams its X through a ring of D steps in LDS
+// (the DMA for step j + D - 1 is issued as soon as step j has arrived).  The
+// P of step k is copied raw into LDS by waves 0..3 (one DMA instruction each)
+// during step k - D - 1, converted to operand form by waves 0 and 1 at the
+// end of step k - 1, and published by the workgroup barrier that ends that
+// step.  Nothing waits for a load issued in the same step.
+//
 // Minimum waves per SIMD the register allocation must allow: two 5-wave
-// workgroups per CU need 3 (at most 168 VGPRs); with 4-wave workgroups the
-// LDS already limits a CU to two workgroups, i.e. 2 waves per SIMD.
+// workgroups per CU need 3 (at most 168 VGPRs); with 4-wave workgroups two
+// per CU need 2.
 constexpr int waves_per_eu(int nw) { return nw == 5 ? 3 : 2; }
 
 template <int NW, int D, bool kAddend>
@@ -204,19 +227,15 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu(NW)))) void projection_kernel(
     const float *__restrict__ grad_proj, const float *__restrict__ grad_r,
     const float *__restrict__ r, uint16_t *__restrict__ dx, float *__restrict__ ws,
     const uint16_t *__restrict__ addend, int64_t T, int64_t K, int64_t L) {
-    static_assert(D >= 2 && D <= 4, "ring depth");
+    static_assert(NW >= 4, "waves 0..3 copy P");
+    static_assert(D >= 2 && D <= 3, "ring depth");
+    constexpr int R = D + 1;  // raw P buffers; the P of step k is requested in step k - R
     __shared__ f32x4 xring[NW][D][4][kWave];
-    __shared__ ChunkLds chunk[2];
+    __shared__ RawStep praw[R];
+    __shared__ StepP pop[2];
     constexpr int kThreads = NW * kWave;
-    constexpr int kItems = kChunk * (kProjCols / 4);  // float4 of P per chunk
-    constexpr int kItemsPerThread = (kItems + kThreads - 1) / kThreads;
-    // VMEM instructions issued after the X DMA of step j and before the wait
-    // for it, in steady state.  Each step issues, in this order: [4 addend
-    // loads] 4 DMA loads (for step + D - 1), 4 dX stores.  The DMA of step j
-    // is issued in step j - D + 1; after it come that step's 4 stores and the
-    // D - 2 full steps in between.  Other VMEM instructions (P staging) only
-    // add to the count, which makes the wait stricter, never looser.
-    constexpr int kAfter = 4 + (D - 2) * (8 + (kAddend ? 4 : 0));
+    constexpr int kConvItems = kStepRows * (kProjCols / 4);  // float4 of P per step
+    static_assert(kConvItems + kStepRows <= kThreads, "one conversion item per thread");
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -228,40 +247,167 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu(NW)))) void projection_kernel(
     const bool active = col < K;
     const int64_t row0 = static_cast<int64_t>(s) * L;
     const int64_t row1 = (row0 + L < T) ? row0 + L : T;
+    const int slab_rows = static_cast<int>(row1 - row0);  // <= L < 2^31
+    const int nsteps = (slab_rows + kStepRows - 1) / kStepRows;
     const float kf = static_cast<float>(K);
+    const int ki = static_cast<int>(K);    // K <= 2^22
+    const int kwi = static_cast<int>(kw);  // kw < K + NW * 64
 
-    // Per-lane byte offsets inside one step (rows 4g + r, columns 4c..4c+3);
-    // inactive columns get an offset outside every range, so their loads read
-    // zeros and their stores are dropped.
+    // VMEM instructions issued after the X DMA of step j and before the wait
+    // for it, in steady state.  Each step issues, in this order: [4 addend
+    // loads] [1 P DMA, waves 0..3] 4 X DMA (for step j + D - 1), 4 dX stores.
+    // The DMA of step j is issued in step j - D + 1; after it come that
+    // step's 4 stores and the D - 2 full steps in between.
+    const bool copies_p = wave < 4;
+    auto wait_x = [&](int j) {
+        if (j < D - 1) {
+            wait_vmcnt<0>();
+        } else if constexpr (D == 2) {
+            wait_vmcnt<4>();
+        } else {
+            constexpr int kBase = 4 + (D - 2) * (8 + (kAddend ? 4 : 0));
+            if (copies_p)
+                wait_vmcnt<kBase + (D - 2)>();
+            else
+                wait_vmcnt<kBase>();
+        }
+    };
+
+    // Per-lane byte offsets inside one row group of a step (row 4g, columns
+    // 4c..4c+3); inactive columns get an offset outside every range, so their
+    // loads read zeros and their stores are dropped.  Row r = 0..3 of the
+    // group is addressed through a buffer resource of its own, based at row
+    // t0 + r and column kw, whose range ends at the slab end or 16 rows on
+    // (whichever comes first): every access of the step lies within 13 rows,
+    // and a row past the slab end lies outside the range.  The per-lane
+    // offset is the same for all four rows; the hardware range check covers
+    // it (the scalar offset, which is not checked, stays zero).
     const uint32_t xoff = active ? static_cast<uint32_t>((4 * g * K + 4 * c16) * 4) : kOutOfRange;
     const uint32_t doff = active ? static_cast<uint32_t>((4 * g * K + 4 * c16) * 2) : kOutOfRange;
-    // Byte offsets of rows r = 0..3 of a step.  They go into the per-lane
-    // (VGPR) offset, which the hardware range check covers; the scalar offset
-    // is not range-checked and stays zero.
-    uint32_t xoffr[4], doffr[4];
+    // Byte range of a row resource: rows_left rows of the slab remain from
+    // its base row on.  Scalar arithmetic only (readfirstlane marks the
+    // result uniform).
+    auto range_bytes = [&](int rows_left, int elem_bytes) {
+        const int rl = rows_left < 0 ? 0 : (rows_left > kStepRows ? kStepRows : rows_left);
+        const int n = rl * ki - kwi;
+        return __builtin_amdgcn_readfirstlane(n > 0 ? n * elem_bytes : 0);
+    };
+    auto step_rows = [&](int rows_left) {
+        return __builtin_amdgcn_readfirstlane(
+            rows_left < 0 ? 0 : (rows_left > kStepRows ? kStepRows : rows_left));
+    };
+    const int64_t row_bytes_x = K * 4;   // one row of X
+    const int64_t row_bytes_d = K * 2;   // one row of dX or the addend
+
+    // ---- X ring: step j's 16 rows go to stage j % D of this wave's ring.
+    // xs points at row 0, column kw of the step; rows_left counts the slab
+    // rows from there on.
+    const uint32_t ring_base =
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&xring[wave][0][0][0]));
+    auto issue_x = [&](const char *xs, int rows_left, int stage) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        xoffr[rr] = xoff + static_cast<uint32_t>(rr * K * 4);
-        doffr[rr] = doff + static_cast<uint32_t>(rr * K * 2);
+        for (int rr = 0; rr < 4; ++rr) {
+            const __amdgpu_buffer_rsrc_t xrs =
+                make_rsrc32(xs + rr * row_bytes_x, range_bytes(rows_left - rr, 4));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xrs, (MHCPB_LDS void *)(&xring[wave][stage][rr][0]), 16, xoff, 0, 0, MHCPB_X_AUX);
+        }
+    };
+
+    // ---- raw P of step k into praw[k % R]: waves 0 and 1 copy rows 0..7 and
+    // 8..15 of grad_proj (16 bytes per lane), waves 2 and 3 grad_r and r (4
+    // bytes per lane).  Rows past the slab end read as zeros.  src is this
+    // wave's source at row 0 of the step (grad_proj, grad_r or r).
+    const int64_t p_step_bytes = (wave < 2) ? kStepRows * kProjStride * 4 : kStepRows * 4;
+    const char *p_src = (wave < 2) ? reinterpret_cast<const char *>(grad_proj + row0 * kProjStride)
+                                   : reinterpret_cast<const char *>((wave == 2 ? grad_r : r) + row0);
+    auto issue_p = [&](const char *src, int rows_left, int k) {
+        const int rl = step_rows(rows_left);
+        RawStep &dst = praw[k % R];
+        if (wave < 2) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                make_rsrc32(src, rl * kProjStride * 4), (MHCPB_LDS void *)(&dst.p[wave * kWave]), 16,
+                static_cast<uint32_t>((wave * kWave + lane) * 16), 0, 0, 0);
+        } else if (wave < 4) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                make_rsrc32(src, rl * 4), (MHCPB_LDS void *)(wave == 2 ? dst.gr : dst.r), 4,
+                static_cast<uint32_t>(lane * 4), 0, 0, 0);
+        }
+    };
+
+    // ---- operand form of the P of step k, from praw[k % R] into pop[k & 1]:
+    // threads 0..95 split one float4 of P each, threads 96..111 compute the
+    // RMS coefficient grad_r / (r K) of one row in FP32 (zero past the slab).
+    auto convert = [&](int k) {
+        const RawStep &src = praw[k % R];
+        const StepP &d = pop[k & 1];
+        if (tid < kConvItems) {
+            const int rr = tid / (kProjCols / 4);
+            const int q = tid % (kProjCols / 4);
+            f32x4 v = lds_read_b128(lds_addr(&src.p[rr * (kProjStride / 4) + q]));
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v)::"memory");
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t pk = tf32_split_packed(v[e]);
+                hi[e] = pk & 0xFFFFu;
+                lo[e] = pk >> 16;
+                const int j = 4 * q + e;
+                lds_write_u16(lds_addr(d.pb + (0 * kJPad + j) * kPbStride + rr), hi[e]);
+                lds_write_u16(lds_addr(d.pb + (1 * kJPad + j) * kPbStride + rr), lo[e]);
+            }
+            const uint32_t dst = lds_addr(d.pa + rr * kPaStride + 4 * q);
+            lds_write_u128(dst, u32x4{hi[0] * 0x10001u, hi[1] * 0x10001u, hi[2] * 0x10001u,
+                                      hi[3] * 0x10001u});
+            lds_write_u128(dst + kJPad * 4, u32x4{lo[0] * 0x10001u, lo[1] * 0x10001u,
+                                                  lo[2] * 0x10001u, lo[3] * 0x10001u});
+        } else if (tid < kConvItems + kStepRows) {
+            const int rr = tid - kConvItems;
+            float grv = lds_read_f32(lds_addr(&src.gr[rr]));
+            float rv = lds_read_f32(lds_addr(&src.r[rr]));
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(grv), "+v"(rv)::"memory");
+            const bool in_slab = kStepRows * k + rr < slab_rows;
+            lds_write_u32(lds_addr(d.c + rr), __float_as_uint(in_slab ? grv / (rv * kf) : 0.f));
+        }
+    };
+
+    // The X of the first D - 1 steps and the P of the first R steps are
+    // requested before anything else, so that their latency overlaps the W
+    // loads below.
+    const char *x_next = reinterpret_cast<const char *>(x + row0 * K + kw);
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) {
+        issue_x(x_next, slab_rows - kStepRows * j, j);
+        x_next += kStepRows * row_bytes_x;
+    }
+    const char *p_next = p_src;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        issue_p(p_next, slab_rows - kStepRows * k, k);
+        p_next += p_step_bytes;
     }
 
-    // W side of the dX product, kept as unique halves: for column variant i
-    // and MFMA u the lane holds (Wh_j | Wl_j << 16, Wh_j1 | Wl_j1 << 16),
-    // j = 8u + 2g; the MFMA operand [Wh_j Wh_j Wh_j1 Wh_j1 Wl_j Wl_j Wl_j1
-    // Wl_j1] is rebuilt from them with v_perm right before use.
-    u32x2 bwu[4][3];
+    // W side of the dX product: for column variant i and j block b the lane
+    // holds the packed (hi | lo << 16) TF32 split of W[j][col + i] for
+    // j = 16b + 4g .. 16b + 4g + 3 (zero for j >= 24).
+    u32x4 bw[4][2];
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-        const int j = 8 * u + 2 * g;
-        float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), w1 = w0;
-        if (active) {
-            w0 = *reinterpret_cast<const float4 *>(w + j * K + col);
-            w1 = *reinterpret_cast<const float4 *>(w + (j + 1) * K + col);
+    for (int b = 0; b < 2; ++b) {
+        float wv[4][4];  // [e][i]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 16 * b + 4 * g + e;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (active && j < kProjCols) v = *reinterpret_cast<const float4 *>(w + j * K + col);
+            wv[e][0] = v.x;
+            wv[e][1] = v.y;
+            wv[e][2] = v.z;
+            wv[e][3] = v.w;
         }
-        const float a0[4] = {w0.x, w0.y, w0.z, w0.w};
-        const float a1[4] = {w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bwu[i][u] = u32x2{tf32_split_packed(a0[i]), tf32_split_packed(a1[i])};
+        for (int i = 0; i < 4; ++i)
+            bw[i][b] = u32x4{tf32_split_packed(wv[0][i]), tf32_split_packed(wv[1][i]),
+                             tf32_split_packed(wv[2][i]), tf32_split_packed(wv[3][i])};
     }
 
     f32x4 accw[4][2];
@@ -270,206 +416,145 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu(NW)))) void projection_kernel(
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) accw[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- P staging: rows [c0, c0 + kChunk) of the slab, loaded to registers
-    // with range-checked buffer loads (rows past the slab read zeros) ...
-    float4 pv[kItemsPerThread];
-    float grv = 0.f, rv = 0.f;
-    auto stage_load = [&](int64_t c0) {
-        const int64_t rows_left = row1 - c0;
-        const __amdgpu_buffer_rsrc_t prs =
-            make_rsrc(grad_proj + c0 * kProjStride, rows_left * kProjStride * 4);
-        // Every thread issues every load (threads past the item count read an
-        // out-of-range offset, i.e. zeros): no divergent loads here.
-#pragma unroll
-        for (int it = 0; it < kItemsPerThread; ++it) {
-            const int item = tid + it * kThreads;
-            const int rr = item / (kProjCols / 4);
-            const int q = item % (kProjCols / 4);
-            const uint32_t off = item < kItems
-                                     ? static_cast<uint32_t>((rr * kProjStride + 4 * q) * 4)
-                                     : kOutOfRange;
-            pv[it] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0));
-        }
-        const __amdgpu_buffer_rsrc_t grs = make_rsrc(grad_r + c0, rows_left * 4);
-        const __amdgpu_buffer_rsrc_t rrs = make_rsrc(r + c0, rows_left * 4);
-        const uint32_t toff = tid < kChunk ? static_cast<uint32_t>(tid * 4) : kOutOfRange;
-        grv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grs, toff, 0, 0));
-        rv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrs, toff, 0, 0));
-    };
-    // ... then split and written in both LDS layouts, with the RMS
-    // coefficient grad_r / (r K) in FP32 (zero for rows past the slab).
-    auto stage_store = [&](const ChunkLds &d, int64_t c0) {
-#pragma unroll
-        for (int it = 0; it < kItemsPerThread; ++it) {
-            const int item = tid + it * kThreads;
-            if (item < kItems) {
-                const int rr = item / (kProjCols / 4);
-                const int q = item % (kProjCols / 4);
-                const float vv[4] = {pv[it].x, pv[it].y, pv[it].z, pv[it].w};
-                uint32_t pk[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pk[e] = tf32_split_packed(vv[e]);
-                    lds_write_u32(lds_addr(d.pt + (4 * q + e) * kPtStride + rr), pk[e]);
-                }
-                const uint32_t dst = lds_addr(d.ps + rr * kPsStride + 4 * q);
-                lds_write_u64(dst, u32x2{pk[0], pk[1]});
-                lds_write_u64(dst + 8, u32x2{pk[2], pk[3]});
-            }
-        }
-        if (tid < kChunk)
-            lds_write_u32(lds_addr(d.c + tid),
-                          __float_as_uint((c0 + tid < row1) ? grv / (rv * kf) : 0.f));
-    };
-
-    // ---- X ring: step j's 16 rows go to stage j % D of this wave's ring.
-    const uint32_t ring_base =
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&xring[wave][0][0][0]));
-    auto issue_x = [&](int64_t t0, int stage) {
-        const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + t0 * K + kw, ((row1 - t0) * K - kw) * 4);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xrs, (MHCPB_LDS void *)(&xring[wave][stage][rr][0]), 16, xoffr[rr],
-                0, 0, MHCPB_X_AUX);
-    };
-
-    // The dW operand rows j = 24..31 of both P buffers are zero padding.
-    for (int i = tid; i < 2 * (32 - kProjCols) * kPtStride; i += kThreads) {
-        const int buf = i / ((32 - kProjCols) * kPtStride);
-        lds_write_u32(lds_addr(chunk[buf].pt + kProjCols * kPtStride +
-                               i % ((32 - kProjCols) * kPtStride)),
-                      0u);
+    // The j = 24..31 entries of both operand buffers are zero padding.
+    constexpr int kPadJ = kJPad - kProjCols;
+    for (int i = tid; i < 2 * kStepRows * 2 * kPadJ; i += kThreads) {
+        const int buf = i / (kStepRows * 2 * kPadJ);
+        const int k = i % (kStepRows * 2 * kPadJ);
+        const int row = k / (2 * kPadJ), rest = k % (2 * kPadJ);
+        const int part = rest / kPadJ, jj = kProjCols + rest % kPadJ;
+        lds_write_u32(lds_addr(pop[buf].pa + row * kPaStride + part * kJPad + jj), 0u);
+    }
+    for (int i = tid; i < 2 * 2 * kPadJ * kPbStride; i += kThreads) {
+        const int buf = i / (2 * kPadJ * kPbStride);
+        const int k = i % (2 * kPadJ * kPbStride);
+        const int part = k / (kPadJ * kPbStride);
+        const int off = k % (kPadJ * kPbStride);
+        lds_write_u16(lds_addr(pop[buf].pb + (part * kJPad + kProjCols) * kPbStride + off), 0u);
     }
 
-    const int64_t nchunks = (row1 - row0 + kChunk - 1) / kChunk;
-    if (nchunks > 0) {
-        stage_load(row0);
-        stage_store(chunk[0], row0);
-#pragma unroll
-        for (int j = 0; j < D - 1; ++j) issue_x(row0 + 16 * j, j);
-    }
+    // Raw P of the first R steps in place and visible, then step 0 in
+    // operand form.
+    wait_vmcnt<0>();
+    lds_barrier();
+    convert(0);
     lds_barrier();
 
-    int j = 0;  // step index within the slab
-    for (int64_t ch = 0; ch < nchunks; ++ch) {
-        const int64_t c0 = row0 + ch * kChunk;
-        const ChunkLds &cur = chunk[ch & 1];
-        // The next chunk's P rows (past the slab end they read as zeros and
-        // are never used), loaded now and staged after this chunk's steps.
-        stage_load(c0 + kChunk);
+    char *d_cur = reinterpret_cast<char *>(dx + row0 * K + kw);
+    const char *a_cur = reinterpret_cast<const char *>(addend + row0 * K + kw);
+    for (int j = 0; j < nsteps; ++j) {
+        const int rows_left = slab_rows - kStepRows * j;
+        // Wait for this step's X, read it, then reuse the stage of the
+        // previous step for the step D - 1 ahead.  Steps past the slab end
+        // are still requested (they read zeros; their stores fall outside the
+        // range), which keeps every step's VMEM count identical.
+        wait_x(j);
+        const StepP &cur = pop[j & 1];
+        const uint32_t xa = ring_base + static_cast<uint32_t>((((j % D) * 4) * kWave + lane) * 16);
+        // Every LDS operand of this step in one batch: X (4 rows), the RMS
+        // coefficients of rows 4g..4g+3, the dX P operands (token c16, part
+        // p, j = 16b + 4g .. +3) and the dW P operands (part p, j = 16b +
+        // c16, rows 4g .. 4g+3; entries j >= 24 are zero).
+        f32x4 xc[4];
 #pragma unroll
-        for (int stl = 0; stl < kStepsPerChunk; ++stl, ++j) {
-            // Steps are never skipped: in a ragged last chunk a step past the
-            // slab reads zeros and its stores fall outside the range, which
-            // keeps every step's VMEM count identical.
-            const int64_t t0 = c0 + 16 * stl;
-            // Wait for this step's X, read it, then reuse the stage of the
-            // previous step for the step D - 1 ahead (always issued, so the
-            // count of later VMEM instructions is the same every step).
-            if (j < D - 1)
-                wait_vmcnt<0>();
-            else
-                wait_vmcnt<kAfter>();
-            const int stage = j % D;
-            const uint32_t xa = ring_base + static_cast<uint32_t>(((stage * 4) * kWave + lane) * 16);
-            // Every LDS operand of this step in one batch: X (4 rows), the RMS
-            // coefficients of rows 4g..4g+3, the dX P operands (token c16,
-            // j = 8u + 2g, j + 1) and the dW P operands (j = 16 jb + c16,
-            // tokens 4g..4g+3; rows j >= 24 are zero).
-            f32x4 xc[4];
+        for (int rr = 0; rr < 4; ++rr) xc[rr] = lds_read_b128(xa + rr * kWave * 16);
+        f32x4 cc = lds_read_b128(lds_addr(cur.c + 4 * g));
+        u32x4 pa[2][2];  // [part][block]
+        u32x2 pbv[2][2];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) xc[rr] = lds_read_b128(xa + rr * kWave * 16);
-            f32x4 cc = lds_read_b128(lds_addr(cur.c + 16 * stl + 4 * g));
-            u32x2 pav[3];
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
-            for (int u = 0; u < 3; ++u)
-                pav[u] = lds_read_u64(lds_addr(cur.ps + (16 * stl + c16) * kPsStride + 8 * u + 2 * g));
-            u32x4 pbv[2];
+            for (int b = 0; b < 2; ++b) {
+                pa[p][b] = lds_read_u128(
+                    lds_addr(cur.pa + c16 * kPaStride + p * kJPad + 16 * b + 4 * g));
+                pbv[p][b] = lds_read_u64(
+                    lds_addr(cur.pb + (p * kJPad + 16 * b + c16) * kPbStride + 4 * g));
+            }
+        // The wait names every register the reads above return, so no use
+        // of them can be scheduled before the data has arrived.
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
+                       "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]), "+v"(pa[1][1]),
+                       "+v"(pbv[0][0]), "+v"(pbv[0][1]), "+v"(pbv[1][0]), "+v"(pbv[1][1])::"memory");
+        uint2 av[4];
+        if constexpr (kAddend) {
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-                pbv[jb] = lds_read_u128(lds_addr(cur.pt + (16 * jb + c16) * kPtStride + 16 * stl + 4 * g));
-            // The wait names every register the reads above return, so no use
-            // of them can be scheduled before the data has arrived.
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc), "+v"(pav[0]),
-                           "+v"(pav[1]), "+v"(pav[2]), "+v"(pbv[0]), "+v"(pbv[1])::"memory");
-            uint2 av[4];
-            const __amdgpu_buffer_rsrc_t drs = make_rsrc(dx + t0 * K + kw, ((row1 - t0) * K - kw) * 2);
-            if constexpr (kAddend) {
+            for (int rr = 0; rr < 4; ++rr) {
                 const __amdgpu_buffer_rsrc_t ars =
-                    make_rsrc(addend + t0 * K + kw, ((row1 - t0) * K - kw) * 2);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ars, doffr[rr], 0, 0);
-                    av[rr] = make_uint2(v.x, v.y);
-                }
+                    make_rsrc32(a_cur + rr * row_bytes_d, range_bytes(rows_left - rr, 2));
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ars, doff, 0, 0);
+                av[rr] = make_uint2(v.x, v.y);
             }
-            compiler_fence();
-            issue_x(t0 + 16 * (D - 1), (j + D - 1) % D);
-            compiler_fence();
-
-            const float ce[4] = {cc[0], cc[1], cc[2], cc[3]};
-            u32x4 pa[3], pb[2][2];
-#pragma unroll
-            for (int u = 0; u < 3; ++u) pa[u] = u32x4{pav[u].x, pav[u].y, pav[u].x, pav[u].y};
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                pb[jb][0] = u32x4{pbv[jb].x, pbv[jb].x, pbv[jb].y, pbv[jb].y};
-                pb[jb][1] = u32x4{pbv[jb].z, pbv[jb].z, pbv[jb].w, pbv[jb].w};
-            }
-
-            uint32_t packed[4][2];  // dX of row 4g + r, columns (0,1) and (2,3)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // dX for column variant i: the RMS term c_t * x in FP32, then
-                // the 96 exact partial products.
-                f32x4 acc = f32x4{ce[0] * xc[0][i], ce[1] * xc[1][i], ce[2] * xc[2][i],
-                                  ce[3] * xc[3][i]};
-#pragma unroll
-                for (int u = 0; u < 3; ++u) acc = mfma(pa[u], dup_halves(bwu[i][u]), acc);
-
-                // dW: x of column variant i split into BF16 hi/lo; for token
-                // pair h the operand is [xh_a xh_a xl_a xl_a xh_b xh_b xl_b xl_b].
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    uint32_t ha, hb2;
-                    float la, lb;
-                    tf32_split(xc[2 * h][i], ha, la);
-                    tf32_split(xc[2 * h + 1][i], hb2, lb);
-                    const u32x4 ax = u32x4{
-                        __builtin_amdgcn_perm(ha, ha, 0x07060706u),
-                        __builtin_amdgcn_perm(__float_as_uint(la), __float_as_uint(la), 0x07060706u),
-                        __builtin_amdgcn_perm(hb2, hb2, 0x07060706u),
-                        __builtin_amdgcn_perm(__float_as_uint(lb), __float_as_uint(lb), 0x07060706u)};
-#pragma unroll
-                    for (int jb = 0; jb < 2; ++jb) accw[i][jb] = mfma(ax, pb[jb][h], accw[i][jb]);
-                }
-
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    float d = acc[rr];
-                    if constexpr (kAddend) {
-                        const uint32_t word = (i < 2) ? av[rr].x : av[rr].y;
-                        d += bf16_to_f32((i & 1) ? (word >> 16) : (word & 0xFFFFu));
-                    }
-                    if (i & 1)
-                        packed[rr][i >> 1] = pack_bf16x2(__uint_as_float(packed[rr][i >> 1]), d);
-                    else
-                        packed[rr][i >> 1] = __float_as_uint(d);
-                }
-            }
-            // One rounding to BF16 per element (above), then 8-byte
-            // range-checked stores: rows past the slab end are dropped.
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[rr][0], packed[rr][1]}, drs,
-                                                      doffr[rr], 0, MHCPB_DX_AUX);
+            a_cur += kStepRows * row_bytes_d;
         }
-        stage_store(chunk[(ch + 1) & 1], c0 + kChunk);
+        compiler_fence();
+        issue_p(p_next, rows_left - kStepRows * R, j + R);
+        issue_x(x_next, rows_left - kStepRows * (D - 1), (j + D - 1) % D);
+        p_next += p_step_bytes;
+        x_next += kStepRows * row_bytes_x;
+        compiler_fence();
+
+        const float ce[4] = {cc[0], cc[1], cc[2], cc[3]};
+        u32x4 pb[2][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                pb[p][b] = u32x4{pbv[p][b].x, pbv[p][b].y, pbv[p][b].x, pbv[p][b].y};
+
+        uint32_t packed[4][2];  // dX of row 4g + r, columns (0,1) and (2,3)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // dX for column variant i: the RMS term c_t * x in FP32, then
+            // the 96 exact partial products.
+            f32x4 acc = f32x4{ce[0] * xc[0][i], ce[1] * xc[1][i], ce[2] * xc[2][i],
+                              ce[3] * xc[3][i]};
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) acc = mfma(pa[p][b], bw[i][b], acc);
+
+            // dW: x of column variant i split into BF16 hi/lo, packed
+            // [hi r0..r3 | lo r0..r3], against each P part.
+            uint32_t hb[4];
+            float lo[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) tf32_split(xc[rr][i], hb[rr], lo[rr]);
+            const u32x4 ax = u32x4{hi_halves(hb[0], hb[1]), hi_halves(hb[2], hb[3]),
+                                   hi_halves(__float_as_uint(lo[0]), __float_as_uint(lo[1])),
+                                   hi_halves(__float_as_uint(lo[2]), __float_as_uint(lo[3]))};
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) accw[i][b] = mfma(ax, pb[p][b], accw[i][b]);
+
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                float d = acc[rr];
+                if constexpr (kAddend) {
+                    const uint32_t word = (i < 2) ? av[rr].x : av[rr].y;
+                    d += bf16_to_f32((i & 1) ? (word >> 16) : (word & 0xFFFFu));
+                }
+                if (i & 1)
+                    packed[rr][i >> 1] = pack_bf16x2(__uint_as_float(packed[rr][i >> 1]), d);
+                else
+                    packed[rr][i >> 1] = __float_as_uint(d);
+            }
+        }
+        // One rounding to BF16 per element (above), then 8-byte range-checked
+        // stores: rows past the slab end are dropped.
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const __amdgpu_buffer_rsrc_t drs =
+                make_rsrc32(d_cur + rr * row_bytes_d, range_bytes(rows_left - rr, 2));
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[rr][0], packed[rr][1]}, drs, doff,
+                                                  0, MHCPB_DX_AUX);
+        }
+        d_cur += kStepRows * row_bytes_d;
+        convert(j + 1);
         lds_barrier();
     }
-    // Drain the X DMA still in flight (steps past the slab end) before the
+    // Drain the DMA still in flight (steps past the slab end) before the
     // workgroup's LDS can be released.
     wait_vmcnt<0>();
 
@@ -529,11 +614,11 @@ hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream)
 // same order whatever the workgroup width, so every shape gives the same bits.
 // With 8 or fewer splits a 5-wave workgroup (320 columns) makes the grid one
 // full round of two workgroups per CU at K = 20480 on 256 CUs; with more
-// splits the grid is several rounds anyway and 4-wave workgroups stream
-// better.
+// splits the grid is several rounds anyway and 4-wave workgroups (two per CU,
+// two waves per SIMD) stream better.
 hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream) {
-    if (p.S <= 8) return launch_projection_t<5, 3>(p, a, stream);
-    return launch_projection_t<4, 3>(p, a, stream);
+    if (p.S <= 8) return launch_projection_t<5, 2>(p, a, stream);
+    return launch_projection_t<4, 2>(p, a, stream);
 }
 
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream) {
