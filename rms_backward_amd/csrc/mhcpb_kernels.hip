@@ -97,6 +97,28 @@ __device__ __forceinline__ uint32_t tf32_split_packed(float v) {
     return ((u & 0x7F800000u) == 0x7F800000u) ? quiet : finite;
 }
 
+// The split of a P value for the staging wave: like tf32_split_packed for
+// finite values; a NaN is first replaced by the canonical quiet NaN (so the
+// rounding cannot carry it out of the exponent), and an infinity keeps an
+// infinite high part (its low part is then NaN).  Either way every product
+// with the value is non-finite, as IEEE arithmetic on the TF32 value gives.
+__device__ __forceinline__ uint32_t tf32_split_packed_p(float v) {
+    const float q = (v != v) ? __uint_as_float(0x7FC00000u) : v;
+    uint32_t hb;
+    float lo;
+    tf32_split(q, hb, lo);
+    return __builtin_amdgcn_perm(__float_as_uint(lo), hb, 0x07060302u);
+}
+
+// Both 16-bit halves equal to the low (sel = 0x05040504) or the high
+// (sel = 0x07060706) half of a.
+__device__ __forceinline__ uint32_t dup_low_half(uint32_t a) {
+    return __builtin_amdgcn_perm(a, a, 0x05040504u);
+}
+__device__ __forceinline__ uint32_t dup_high_half(uint32_t a) {
+    return __builtin_amdgcn_perm(a, a, 0x07060706u);
+}
+
 // Upper halves of two 32-bit words: (a >> 16) | (b & 0xFFFF0000).
 __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07060302u);
@@ -151,6 +173,15 @@ __device__ __forceinline__ void lds_write_u16(uint32_t addr, uint32_t v) {
     asm volatile("ds_write_b16 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
+// Writes the high 16 bits of v.
+__device__ __forceinline__ void lds_write_u16_hi(uint32_t addr, uint32_t v) {
+    asm volatile("ds_write_b16_d16_hi %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ void lds_write_u64(uint32_t addr, u32x2 v) {
+    asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
@@ -168,6 +199,27 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // Barrier for LDS data only (no wait on outstanding global traffic).
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Adds one to the LDS counter at addr once this wave's earlier LDS accesses
+// have completed (lane 0 does the add).
+__device__ __forceinline__ void lds_signal(uint32_t addr, int lane) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(1u) : "memory");
+}
+
+// Waits until the LDS counter at addr is at least target.  The callers'
+// counters always get there, within a few steps' time; the bound (2^16
+// polls, a few milliseconds) only keeps a broken invariant from hanging the
+// GPU.
+constexpr int kMaxPolls = 1 << 16;
+__device__ __forceinline__ void lds_wait_at_least(uint32_t addr, uint32_t target) {
+    for (int poll = 0; poll < kMaxPolls; ++poll) {
+        uint32_t v;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+        if (__builtin_amdgcn_readfirstlane(v) >= target) return;
+        __builtin_amdgcn_s_sleep(1);
+    }
 }
 
 // Rows per step (one MFMA row block) and the LDS layouts of P.
@@ -191,15 +243,22 @@ struct RawStep {
 //  pb[part][j][row]: the part, as the dW product reads it (4 consecutive rows);
 //  c[row]: grad_r / (r K).
 // Entries with j >= 24 are zero and never written after the first clear.
-struct StepP {
+struct alignas(16) StepP {
     uint32_t pa[kStepRows * kPaStride];
     uint16_t pb[2 * kJPad * kPbStride];
     float c[kStepRows];
 };
 
-// Kernel 1.  A workgroup of NW waves owns NW * 64 columns of one slab.  Per
-// step a wave handles 16 rows x 64 columns: lane l (c = l % 16, g = l / 16)
-// holds x[t0 + 4g + r][kw + 4c + i] for r, i in 0..3.
+// Operand slots in rotation, and how many steps ahead of its conversion the
+// producer requests the raw P of a step.
+constexpr int kSlots = 4;
+constexpr int kRawAhead = 2;
+constexpr int kRawBufs = kRawAhead + 1;
+
+// Kernel 1.  A workgroup has NW compute waves, which own NW * 64 columns of
+// one slab, and one producer wave.  Per step a compute wave handles 16 rows x
+// 64 columns: lane l (c = l % 16, g = l / 16) holds x[t0 + 4g + r][kw + 4c + i]
+// for r, i in 0..3.
 //  dX: C_i[e] = dX[t0 + 4g + e][kw + 4c + i] = c_t x + the products of the P
 //      parts (token t0 + l%16) with the W parts (column kw + 4c + i): per
 //      MFMA (P part p, j block b) lane group g covers j = 16b + 4g .. +3 times
@@ -208,183 +267,199 @@ struct StepP {
 //      times TF32(P[j]), j = 16 b + l%16: per MFMA (P part p), lane group g
 //      covers rows 4g .. 4g+3 times (x hi, x lo).
 //
-// Memory pipeline.  Each wave streams its X through a ring of D steps in LDS
-// (the DMA for step j + D - 1 is issued as soon as step j has arrived).  The
-// P of step k is copied raw into LDS by waves 0..3 (one DMA instruction each)
-// during step k - D - 1, converted to operand form by waves 0 and 1 at the
-// end of step k - 1, and published by the workgroup barrier that ends that
-// step.  Nothing waits for a load issued in the same step.
+// Memory pipeline.  Each compute wave streams its X through a two-step ring
+// in LDS: the DMA for step j + 1 is issued as soon as step j has arrived, so
+// one step per wave is in flight.  The producer wave copies the raw P of step
+// k into LDS (DMA) two steps ahead, converts it into operand slot k % 4 and
+// publishes it; it never touches X.
 //
-// Minimum waves per SIMD the register allocation must allow: two 5-wave
-// workgroups per CU need 3 (at most 168 VGPRs); with 4-wave workgroups two
-// per CU need 2.
-constexpr int waves_per_eu(int nw) { return nw == 5 ? 3 : 2; }
-
-template <int NW, int D, bool kAddend>
-__global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu(NW)))) void projection_kernel(
+// Synchronisation.  Each slot has two monotonic LDS counters: "ready" (one
+// count per use, from the producer) and "consumed" (one count per compute
+// wave per use, once its reads of the slot have completed).  A compute wave
+// reads step k once ready[k % 4] reaches k / 4 + 1; the producer writes step
+// k once consumed[k % 4] reaches NW (k / 4), i.e. once every compute wave has
+// read step k - 4 from the slot.  A slot's next use needs the previous one
+// consumed by every wave, so the counts identify the use exactly, and every
+// wait refers to an event of an earlier step, so none can deadlock.  The
+// waits are also bounded, so a broken invariant cannot hang the GPU.  Compute
+// waves never wait for each other.
+//
+// Two workgroups per CU make 12 waves (NW = 5), three per SIMD: the register
+// allocation must stay within 168 VGPRs.
+template <int NW, bool kAddend>
+__global__ __launch_bounds__((NW + 1) * kWave)
+__attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     const float *__restrict__ x, const float *__restrict__ w,
     const float *__restrict__ grad_proj, const float *__restrict__ grad_r,
     const float *__restrict__ r, uint16_t *__restrict__ dx, float *__restrict__ ws,
     const uint16_t *__restrict__ addend, int64_t T, int64_t K, int64_t L) {
-    static_assert(NW >= 4, "waves 0..3 copy P");
-    static_assert(D >= 2 && D <= 3, "ring depth");
-    constexpr int R = D + 1;  // raw P buffers; the P of step k is requested in step k - R
-    __shared__ f32x4 xring[NW][D][4][kWave];
-    __shared__ RawStep praw[R];
-    __shared__ StepP pop[2];
-    constexpr int kThreads = NW * kWave;
-    constexpr int kConvItems = kStepRows * (kProjCols / 4);  // float4 of P per step
-    static_assert(kConvItems + kStepRows <= kThreads, "one conversion item per thread");
+    __shared__ f32x4 xring[NW][2][4][kWave];
+    __shared__ RawStep praw[kRawBufs];
+    __shared__ StepP pop[kSlots];
+    __shared__ uint32_t ready[kSlots], consumed[kSlots];
+    constexpr int kThreads = (NW + 1) * kWave;
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int c16 = lane % 16;
     const int g = lane / 16;
     const int s = blockIdx.y;
-    const int64_t kw = static_cast<int64_t>(blockIdx.x) * (NW * 64) + wave * 64;
-    const int64_t col = kw + 4 * c16;  // first of this lane's 4 columns
-    const bool active = col < K;
     const int64_t row0 = static_cast<int64_t>(s) * L;
     const int64_t row1 = (row0 + L < T) ? row0 + L : T;
     const int slab_rows = static_cast<int>(row1 - row0);  // <= L < 2^31
     const int nsteps = (slab_rows + kStepRows - 1) / kStepRows;
     const float kf = static_cast<float>(K);
-    const int ki = static_cast<int>(K);    // K <= 2^22
-    const int kwi = static_cast<int>(kw);  // kw < K + NW * 64
-
-    // VMEM instructions issued after the X DMA of step j and before the wait
-    // for it, in steady state.  Each step issues, in this order: [4 addend
-    // loads] [1 P DMA, waves 0..3] 4 X DMA (for step j + D - 1), 4 dX stores.
-    // The DMA of step j is issued in step j - D + 1; after it come that
-    // step's 4 stores and the D - 2 full steps in between.
-    const bool copies_p = wave < 4;
-    auto wait_x = [&](int j) {
-        if (j < D - 1) {
-            wait_vmcnt<0>();
-        } else if constexpr (D == 2) {
-            wait_vmcnt<4>();
-        } else {
-            constexpr int kBase = 4 + (D - 2) * (8 + (kAddend ? 4 : 0));
-            if (copies_p)
-                wait_vmcnt<kBase + (D - 2)>();
-            else
-                wait_vmcnt<kBase>();
-        }
-    };
-
-    // Per-lane byte offsets inside one row group of a step (row 4g, columns
-    // 4c..4c+3); inactive columns get an offset outside every range, so their
-    // loads read zeros and their stores are dropped.  Row r = 0..3 of the
-    // group is addressed through a buffer resource of its own, based at row
-    // t0 + r and column kw, whose range ends at the slab end or 16 rows on
-    // (whichever comes first): every access of the step lies within 13 rows,
-    // and a row past the slab end lies outside the range.  The per-lane
-    // offset is the same for all four rows; the hardware range check covers
-    // it (the scalar offset, which is not checked, stays zero).
-    const uint32_t xoff = active ? static_cast<uint32_t>((4 * g * K + 4 * c16) * 4) : kOutOfRange;
-    const uint32_t doff = active ? static_cast<uint32_t>((4 * g * K + 4 * c16) * 2) : kOutOfRange;
-    // Byte range of a row resource: rows_left rows of the slab remain from
-    // its base row on.  Scalar arithmetic only (readfirstlane marks the
-    // result uniform).
-    auto range_bytes = [&](int rows_left, int elem_bytes) {
-        const int rl = rows_left < 0 ? 0 : (rows_left > kStepRows ? kStepRows : rows_left);
-        const int n = rl * ki - kwi;
-        return __builtin_amdgcn_readfirstlane(n > 0 ? n * elem_bytes : 0);
-    };
+    const int ki = static_cast<int>(K);  // K <= 2^22
+    const uint32_t ready_addr = lds_addr(&ready[0]);
+    const uint32_t consumed_addr = lds_addr(&consumed[0]);
+    // Rows of the slab from row 16 k on, clamped to one step.
     auto step_rows = [&](int rows_left) {
         return __builtin_amdgcn_readfirstlane(
             rows_left < 0 ? 0 : (rows_left > kStepRows ? kStepRows : rows_left));
     };
-    const int64_t row_bytes_x = K * 4;   // one row of X
-    const int64_t row_bytes_d = K * 2;   // one row of dX or the addend
 
-    // ---- X ring: step j's 16 rows go to stage j % D of this wave's ring.
-    // xs points at row 0, column kw of the step; rows_left counts the slab
-    // rows from there on.
-    const uint32_t ring_base =
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&xring[wave][0][0][0]));
+    // ---- producer: raw P of step k into praw[k % kRawBufs], two 64-lane DMA
+    // of 16 bytes for the 16 rows of grad_proj and one of 4 bytes each for
+    // grad_r and r.  Rows past the slab end read as zeros.
+    const bool producer = wave == NW;
+    auto issue_raw = [&](int k) {
+        const int rl = step_rows(slab_rows - kStepRows * k);
+        RawStep &d = praw[k % kRawBufs];
+        const int64_t r0 = row0 + static_cast<int64_t>(kStepRows) * k;
+        const __amdgpu_buffer_rsrc_t prs = make_rsrc32(grad_proj + r0 * kProjStride, rl * kProjStride * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (MHCPB_LDS void *)(&d.p[0]), 16,
+                                                 static_cast<uint32_t>(lane * 16), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (MHCPB_LDS void *)(&d.p[kWave]), 16,
+                                                 static_cast<uint32_t>((kWave + lane) * 16), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc32(grad_r + r0, rl * 4),
+                                                 (MHCPB_LDS void *)d.gr, 4,
+                                                 static_cast<uint32_t>(lane * 4), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc32(r + r0, rl * 4),
+                                                 (MHCPB_LDS void *)d.r, 4,
+                                                 static_cast<uint32_t>(lane * 4), 0, 0, 0);
+    };
+    if (producer) {
+#pragma unroll
+        for (int k = 0; k < kRawAhead; ++k) issue_raw(k);
+    }
+
+    // ---- compute waves: X ring, W in registers.
+    const int64_t kw = static_cast<int64_t>(blockIdx.x) * (NW * 64) + (producer ? 0 : wave) * 64;
+    const int kwi = static_cast<int>(kw);  // kw < K + NW * 64
+    const int64_t col = kw + 4 * c16;      // first of this lane's 4 columns
+    const bool active = !producer && col < K;
+    // A step is addressed through one buffer resource per tensor, based at
+    // row t0 and column kw, whose range ends at the slab end or 16 rows on,
+    // whichever comes first; lane offsets (row 4g + r, columns 4c..4c+3) go
+    // in the per-lane offset, which the hardware range check covers (the
+    // scalar offset, which is not checked, stays zero).  An element of a
+    // slab row lies in the range because K and the lane's column are
+    // multiples of 4; a row past the slab end lies outside it.  Inactive
+    // columns get an offset outside every range, so their loads read zeros
+    // and their stores are dropped.
+    uint32_t xoff[4], doff[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        xoff[rr] = active ? static_cast<uint32_t>(((4 * g + rr) * K + 4 * c16) * 4) : kOutOfRange;
+        doff[rr] = active ? static_cast<uint32_t>(((4 * g + rr) * K + 4 * c16) * 2) : kOutOfRange;
+    }
+    // Elements of the range of a step resource (times the element size).
+    auto range_elems = [&](int rows_left) {
+        const int rl = rows_left < 0 ? 0 : (rows_left > kStepRows ? kStepRows : rows_left);
+        const int n = rl * ki - kwi;
+        return __builtin_amdgcn_readfirstlane(n > 0 ? n : 0);
+    };
+    const int64_t row_bytes_x = K * 4;  // one row of X
+    const int64_t row_bytes_d = K * 2;  // one row of dX or the addend
+    const int xw = producer ? 0 : wave;
+    const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&xring[xw][0][0][0]));
+    // xs points at row 0, column kw of a step; rows_left counts the slab rows
+    // from there on.
     auto issue_x = [&](const char *xs, int rows_left, int stage) {
+        const __amdgpu_buffer_rsrc_t xrs = make_rsrc32(xs, range_elems(rows_left) * 4);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const __amdgpu_buffer_rsrc_t xrs =
-                make_rsrc32(xs + rr * row_bytes_x, range_bytes(rows_left - rr, 4));
+        for (int rr = 0; rr < 4; ++rr)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xrs, (MHCPB_LDS void *)(&xring[wave][stage][rr][0]), 16, xoff, 0, 0, MHCPB_X_AUX);
-        }
+                xrs, (MHCPB_LDS void *)(&xring[xw][stage][rr][0]), 16, xoff[rr], 0, 0, MHCPB_X_AUX);
     };
-
-    // ---- raw P of step k into praw[k % R]: waves 0 and 1 copy rows 0..7 and
-    // 8..15 of grad_proj (16 bytes per lane), waves 2 and 3 grad_r and r (4
-    // bytes per lane).  Rows past the slab end read as zeros.  src is this
-    // wave's source at row 0 of the step (grad_proj, grad_r or r).
-    const int64_t p_step_bytes = (wave < 2) ? kStepRows * kProjStride * 4 : kStepRows * 4;
-    const char *p_src = (wave < 2) ? reinterpret_cast<const char *>(grad_proj + row0 * kProjStride)
-                                   : reinterpret_cast<const char *>((wave == 2 ? grad_r : r) + row0);
-    auto issue_p = [&](const char *src, int rows_left, int k) {
-        const int rl = step_rows(rows_left);
-        RawStep &dst = praw[k % R];
-        if (wave < 2) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                make_rsrc32(src, rl * kProjStride * 4), (MHCPB_LDS void *)(&dst.p[wave * kWave]), 16,
-                static_cast<uint32_t>((wave * kWave + lane) * 16), 0, 0, 0);
-        } else if (wave < 4) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                make_rsrc32(src, rl * 4), (MHCPB_LDS void *)(wave == 2 ? dst.gr : dst.r), 4,
-                static_cast<uint32_t>(lane * 4), 0, 0, 0);
-        }
-    };
-
-    // ---- operand form of the P of step k, from praw[k % R] into pop[k & 1]:
-    // threads 0..95 split one float4 of P each, threads 96..111 compute the
-    // RMS coefficient grad_r / (r K) of one row in FP32 (zero past the slab).
-    auto convert = [&](int k) {
-        const RawStep &src = praw[k % R];
-        const StepP &d = pop[k & 1];
-        if (tid < kConvItems) {
-            const int rr = tid / (kProjCols / 4);
-            const int q = tid % (kProjCols / 4);
-            f32x4 v = lds_read_b128(lds_addr(&src.p[rr * (kProjStride / 4) + q]));
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v)::"memory");
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t pk = tf32_split_packed(v[e]);
-                hi[e] = pk & 0xFFFFu;
-                lo[e] = pk >> 16;
-                const int j = 4 * q + e;
-                lds_write_u16(lds_addr(d.pb + (0 * kJPad + j) * kPbStride + rr), hi[e]);
-                lds_write_u16(lds_addr(d.pb + (1 * kJPad + j) * kPbStride + rr), lo[e]);
-            }
-            const uint32_t dst = lds_addr(d.pa + rr * kPaStride + 4 * q);
-            lds_write_u128(dst, u32x4{hi[0] * 0x10001u, hi[1] * 0x10001u, hi[2] * 0x10001u,
-                                      hi[3] * 0x10001u});
-            lds_write_u128(dst + kJPad * 4, u32x4{lo[0] * 0x10001u, lo[1] * 0x10001u,
-                                                  lo[2] * 0x10001u, lo[3] * 0x10001u});
-        } else if (tid < kConvItems + kStepRows) {
-            const int rr = tid - kConvItems;
-            float grv = lds_read_f32(lds_addr(&src.gr[rr]));
-            float rv = lds_read_f32(lds_addr(&src.r[rr]));
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(grv), "+v"(rv)::"memory");
-            const bool in_slab = kStepRows * k + rr < slab_rows;
-            lds_write_u32(lds_addr(d.c + rr), __float_as_uint(in_slab ? grv / (rv * kf) : 0.f));
-        }
-    };
-
-    // The X of the first D - 1 steps and the P of the first R steps are
-    // requested before anything else, so that their latency overlaps the W
-    // loads below.
     const char *x_next = reinterpret_cast<const char *>(x + row0 * K + kw);
-#pragma unroll
-    for (int j = 0; j < D - 1; ++j) {
-        issue_x(x_next, slab_rows - kStepRows * j, j);
+    if (!producer) {
+        issue_x(x_next, slab_rows, 0);
         x_next += kStepRows * row_bytes_x;
     }
-    const char *p_next = p_src;
+
+    // The j = 24..31 entries of every operand slot are zero padding; the
+    // counters start at zero.
+    constexpr int kPadJ = kJPad - kProjCols;
+    for (int i = tid; i < kSlots * kStepRows * 2 * kPadJ; i += kThreads) {
+        const int buf = i / (kStepRows * 2 * kPadJ);
+        const int k = i % (kStepRows * 2 * kPadJ);
+        const int row = k / (2 * kPadJ), rest = k % (2 * kPadJ);
+        const int part = rest / kPadJ, jj = kProjCols + rest % kPadJ;
+        lds_write_u32(lds_addr(pop[buf].pa + row * kPaStride + part * kJPad + jj), 0u);
+    }
+    for (int i = tid; i < kSlots * 2 * kPadJ * kPbStride; i += kThreads) {
+        const int buf = i / (2 * kPadJ * kPbStride);
+        const int k = i % (2 * kPadJ * kPbStride);
+        const int part = k / (kPadJ * kPbStride);
+        const int off = k % (kPadJ * kPbStride);
+        lds_write_u16(lds_addr(pop[buf].pb + (part * kJPad + kProjCols) * kPbStride + off), 0u);
+    }
+    if (tid < kSlots) {
+        lds_write_u32(ready_addr + 4 * tid, 0u);
+        lds_write_u32(consumed_addr + 4 * tid, 0u);
+    }
+    lds_barrier();
+
+    if (producer) {
+        // Lane = row * 4 + q converts j = 6q .. 6q + 5 of one row of P into
+        // both operand layouts; lanes 0..15 also compute the RMS coefficient
+        // grad_r / (r K) of row lane in FP32 (zero past the slab end).
+        const int prow = lane / 4;
+        const int pj0 = 6 * (lane % 4);
+        for (int k = 0; k < nsteps; ++k) {
+            issue_raw(k + kRawAhead);
+            // The raw P of step k was requested before that of the kRawAhead
+            // steps after it, 4 DMA instructions each.
+            wait_vmcnt<4 * kRawAhead>();
+            const int slot = k % kSlots;
+            lds_wait_at_least(consumed_addr + 4 * slot, NW * static_cast<uint32_t>(k / kSlots));
+            const RawStep &src = praw[k % kRawBufs];
+            const StepP &d = pop[slot];
+            const uint32_t ra = lds_addr(&src.p[0]) + static_cast<uint32_t>((prow * kProjStride + pj0) * 4);
+            u32x2 v0 = lds_read_u64(ra), v1 = lds_read_u64(ra + 8), v2 = lds_read_u64(ra + 16);
+            float grv = lds_read_f32(lds_addr(&src.gr[lane]));
+            float rv = lds_read_f32(lds_addr(&src.r[lane]));
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(grv), "+v"(rv)::"memory");
+            const uint32_t vv[6] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y};
+            uint32_t pk[6];  // hi | lo << 16
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        issue_p(p_next, slab_rows - kStepRows * k, k);
-        p_next += p_step_bytes;
+            for (int e = 0; e < 6; ++e) pk[e] = tf32_split_packed_p(__uint_as_float(vv[e]));
+            const uint32_t pa_hi = lds_addr(d.pa + prow * kPaStride + pj0);
+            const uint32_t pa_lo = pa_hi + kJPad * 4;
+#pragma unroll
+            for (int e = 0; e < 6; e += 2) {
+                lds_write_u64(pa_hi + 4 * e, u32x2{dup_low_half(pk[e]), dup_low_half(pk[e + 1])});
+                lds_write_u64(pa_lo + 4 * e, u32x2{dup_high_half(pk[e]), dup_high_half(pk[e + 1])});
+            }
+            const uint32_t pb0 = lds_addr(d.pb + pj0 * kPbStride + prow);
+            const uint32_t pb1 = pb0 + kJPad * kPbStride * 2;
+#pragma unroll
+            for (int e = 0; e < 6; ++e) {
+                lds_write_u16(pb0 + e * kPbStride * 2, pk[e]);
+                lds_write_u16_hi(pb1 + e * kPbStride * 2, pk[e]);
+            }
+            if (lane < kStepRows) {
+                const bool in_slab = kStepRows * k + lane < slab_rows;
+                lds_write_u32(lds_addr(d.c + lane), __float_as_uint(in_slab ? grv / (rv * kf) : 0.f));
+            }
+            lds_signal(ready_addr + 4 * slot, lane);
+        }
+        // Drain the copies still in flight before the workgroup's LDS can be
+        // released.
+        wait_vmcnt<0>();
+        return;
     }
 
     // W side of the dX product: for column variant i and j block b the lane
@@ -416,41 +491,24 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu(NW)))) void projection_kernel(
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) accw[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // The j = 24..31 entries of both operand buffers are zero padding.
-    constexpr int kPadJ = kJPad - kProjCols;
-    for (int i = tid; i < 2 * kStepRows * 2 * kPadJ; i += kThreads) {
-        const int buf = i / (kStepRows * 2 * kPadJ);
-        const int k = i % (kStepRows * 2 * kPadJ);
-        const int row = k / (2 * kPadJ), rest = k % (2 * kPadJ);
-        const int part = rest / kPadJ, jj = kProjCols + rest % kPadJ;
-        lds_write_u32(lds_addr(pop[buf].pa + row * kPaStride + part * kJPad + jj), 0u);
-    }
-    for (int i = tid; i < 2 * 2 * kPadJ * kPbStride; i += kThreads) {
-        const int buf = i / (2 * kPadJ * kPbStride);
-        const int k = i % (2 * kPadJ * kPbStride);
-        const int part = k / (kPadJ * kPbStride);
-        const int off = k % (kPadJ * kPbStride);
-        lds_write_u16(lds_addr(pop[buf].pb + (part * kJPad + kProjCols) * kPbStride + off), 0u);
-    }
-
-    // Raw P of the first R steps in place and visible, then step 0 in
-    // operand form.
-    wait_vmcnt<0>();
-    lds_barrier();
-    convert(0);
-    lds_barrier();
-
     char *d_cur = reinterpret_cast<char *>(dx + row0 * K + kw);
     const char *a_cur = reinterpret_cast<const char *>(addend + row0 * K + kw);
     for (int j = 0; j < nsteps; ++j) {
         const int rows_left = slab_rows - kStepRows * j;
-        // Wait for this step's X, read it, then reuse the stage of the
-        // previous step for the step D - 1 ahead.  Steps past the slab end
-        // are still requested (they read zeros; their stores fall outside the
-        // range), which keeps every step's VMEM count identical.
-        wait_x(j);
-        const StepP &cur = pop[j & 1];
-        const uint32_t xa = ring_base + static_cast<uint32_t>((((j % D) * 4) * kWave + lane) * 16);
+        // Wait for this step's X.  Each step issues, in this order: [4 addend
+        // loads] 4 X DMA (for step j + 1), 4 dX stores; the X of step j was
+        // requested in step j - 1 with only that step's 4 stores after it,
+        // so vmcnt(4) covers it.  Step 0 waits for everything.  Steps past
+        // the slab end are still requested (they read zeros; their stores
+        // fall outside the range), which keeps every step's count identical.
+        if (j == 0)
+            wait_vmcnt<0>();
+        else
+            wait_vmcnt<4>();
+        const int slot = j % kSlots;
+        lds_wait_at_least(ready_addr + 4 * slot, static_cast<uint32_t>(j / kSlots + 1));
+        const StepP &cur = pop[slot];
+        const uint32_t xa = ring_base + static_cast<uint32_t>((((j & 1) * 4) * kWave + lane) * 16);
         // Every LDS operand of this step in one batch: X (4 rows), the RMS
         // coefficients of rows 4g..4g+3, the dX P operands (token c16, part
         // p, j = 16b + 4g .. +3) and the dW P operands (part p, j = 16b +
@@ -476,21 +534,20 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu(NW)))) void projection_kernel(
                      : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
                        "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]), "+v"(pa[1][1]),
                        "+v"(pbv[0][0]), "+v"(pbv[0][1]), "+v"(pbv[1][0]), "+v"(pbv[1][1])::"memory");
+        lds_signal(consumed_addr + 4 * slot, lane);
         uint2 av[4];
+        const int d_range = range_elems(rows_left) * 2;
         if constexpr (kAddend) {
+            const __amdgpu_buffer_rsrc_t ars = make_rsrc32(a_cur, d_range);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const __amdgpu_buffer_rsrc_t ars =
-                    make_rsrc32(a_cur + rr * row_bytes_d, range_bytes(rows_left - rr, 2));
-                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ars, doff, 0, 0);
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ars, doff[rr], 0, 0);
                 av[rr] = make_uint2(v.x, v.y);
             }
             a_cur += kStepRows * row_bytes_d;
         }
         compiler_fence();
-        issue_p(p_next, rows_left - kStepRows * R, j + R);
-        issue_x(x_next, rows_left - kStepRows * (D - 1), (j + D - 1) % D);
-        p_next += p_step_bytes;
+        issue_x(x_next, rows_left - kStepRows, (j + 1) & 1);
         x_next += kStepRows * row_bytes_x;
         compiler_fence();
 
@@ -543,19 +600,15 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu(NW)))) void projection_kernel(
         }
         // One rounding to BF16 per element (above), then 8-byte range-checked
         // stores: rows past the slab end are dropped.
+        const __amdgpu_buffer_rsrc_t drs = make_rsrc32(d_cur, d_range);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const __amdgpu_buffer_rsrc_t drs =
-                make_rsrc32(d_cur + rr * row_bytes_d, range_bytes(rows_left - rr, 2));
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[rr][0], packed[rr][1]}, drs, doff,
+        for (int rr = 0; rr < 4; ++rr)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[rr][0], packed[rr][1]}, drs, doff[rr],
                                                   0, MHCPB_DX_AUX);
-        }
         d_cur += kStepRows * row_bytes_d;
-        convert(j + 1);
-        lds_barrier();
     }
-    // Drain the DMA still in flight (steps past the slab end) before the
-    // workgroup's LDS can be released.
+    // Drain the X DMA still in flight (the step past the slab end) before
+    // the workgroup's LDS can be released.
     wait_vmcnt<0>();
 
     // Partial dW of this slab, written once to workspace slab s.  Lane
@@ -594,16 +647,16 @@ __global__ __launch_bounds__(256) void reduce_slabs(const float *__restrict__ ws
     reinterpret_cast<float4 *>(dw)[i] = a;
 }
 
-template <int NW, int D>
+template <int NW>
 hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream) {
     constexpr int cols = NW * 64;
     const dim3 grid(static_cast<unsigned>((p.K + cols - 1) / cols), static_cast<unsigned>(p.S));
-    const dim3 block(NW * kWave);
+    const dim3 block((NW + 1) * kWave);
     if (a.addend)
-        hipLaunchKernelGGL((projection_kernel<NW, D, true>), grid, block, 0, stream, a.x, a.w,
+        hipLaunchKernelGGL((projection_kernel<NW, true>), grid, block, 0, stream, a.x, a.w,
                            a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L);
     else
-        hipLaunchKernelGGL((projection_kernel<NW, D, false>), grid, block, 0, stream, a.x, a.w,
+        hipLaunchKernelGGL((projection_kernel<NW, false>), grid, block, 0, stream, a.x, a.w,
                            a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L);
     return hipGetLastError();
 }
@@ -612,13 +665,11 @@ hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream)
 
 // Launch shape, a performance choice only: each column's dW is summed in the
 // same order whatever the workgroup width, so every shape gives the same bits.
-// With 8 or fewer splits a 5-wave workgroup (320 columns) makes the grid one
-// full round of two workgroups per CU at K = 20480 on 256 CUs; with more
-// splits the grid is several rounds anyway and 4-wave workgroups (two per CU,
-// two waves per SIMD) stream better.
+// Five compute waves and the producer make two workgroups per CU exactly
+// three waves per SIMD; at K = 20480 with 8 splits the grid is one full round
+// of two workgroups per CU on 256 CUs.
 hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream) {
-    if (p.S <= 8) return launch_projection_t<5, 2>(p, a, stream);
-    return launch_projection_t<4, 2>(p, a, stream);
+    return launch_projection_t<5>(p, a, stream);
 }
 
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream) {
