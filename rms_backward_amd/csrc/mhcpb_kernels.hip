@@ -147,6 +147,12 @@ __device__ __forceinline__ u32x4 lds_read_u128(uint32_t addr) {
     return v;
 }
 
+__device__ __forceinline__ uint32_t lds_read_u32(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
 __device__ __forceinline__ float lds_read_f32(uint32_t addr) {
     float v;
     asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
@@ -226,7 +232,7 @@ __device__ __forceinline__ void lds_wait_at_least(uint32_t addr, uint32_t target
 constexpr int kStepRows = 16;
 constexpr int kJPad = 32;                 // j slots per part, 24..31 zero
 constexpr int kPaStride = 2 * kJPad + 4;  // uint32 per row of the dX P operand
-constexpr int kPbStride = kStepRows + 4;  // uint16 per (part, j) row of the dW P operand
+constexpr int kPbJStride = 40;            // uint16 per j of the dW P operand (32 + 8 padding)
 
 // The P of one step as it is stored in HBM, copied by LDS DMA: 16 rows of
 // grad_proj (32 floats each; the last 8 are never read from here), and one
@@ -240,12 +246,13 @@ struct RawStep {
 // The P of one step in operand form (TF32 split into BF16 high and low parts):
 //  pa[row][part * 32 + j]: the part, duplicated in both halves of the word, as
 //      the dX product reads it (4 consecutive j per lane group);
-//  pb[part][j][row]: the part, as the dW product reads it (4 consecutive rows);
+//  pb[j][g][part][r]: the part of row 4g + r, as the dW product reads it (both
+//      parts of 4 consecutive rows in 16 bytes);
 //  c[row]: grad_r / (r K).
 // Entries with j >= 24 are zero and never written after the first clear.
 struct alignas(16) StepP {
     uint32_t pa[kStepRows * kPaStride];
-    uint16_t pb[2 * kJPad * kPbStride];
+    uint16_t pb[kJPad * kPbJStride];
     float c[kStepRows];
 };
 
@@ -398,12 +405,10 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         const int part = rest / kPadJ, jj = kProjCols + rest % kPadJ;
         lds_write_u32(lds_addr(pop[buf].pa + row * kPaStride + part * kJPad + jj), 0u);
     }
-    for (int i = tid; i < kSlots * 2 * kPadJ * kPbStride; i += kThreads) {
-        const int buf = i / (2 * kPadJ * kPbStride);
-        const int k = i % (2 * kPadJ * kPbStride);
-        const int part = k / (kPadJ * kPbStride);
-        const int off = k % (kPadJ * kPbStride);
-        lds_write_u16(lds_addr(pop[buf].pb + (part * kJPad + kProjCols) * kPbStride + off), 0u);
+    for (int i = tid; i < kSlots * kPadJ * kPbJStride; i += kThreads) {
+        const int buf = i / (kPadJ * kPbJStride);
+        const int off = i % (kPadJ * kPbJStride);
+        lds_write_u16(lds_addr(pop[buf].pb + kProjCols * kPbJStride + off), 0u);
     }
     if (tid < kSlots) {
         lds_write_u32(ready_addr + 4 * tid, 0u);
@@ -443,12 +448,12 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                 lds_write_u64(pa_hi + 4 * e, u32x2{dup_low_half(pk[e]), dup_low_half(pk[e + 1])});
                 lds_write_u64(pa_lo + 4 * e, u32x2{dup_high_half(pk[e]), dup_high_half(pk[e + 1])});
             }
-            const uint32_t pb0 = lds_addr(d.pb + pj0 * kPbStride + prow);
-            const uint32_t pb1 = pb0 + kJPad * kPbStride * 2;
+            const uint32_t pb0 = lds_addr(d.pb + pj0 * kPbJStride + (prow / 4) * 8 + prow % 4);
+            const uint32_t pb1 = pb0 + 4 * 2;
 #pragma unroll
             for (int e = 0; e < 6; ++e) {
-                lds_write_u16(pb0 + e * kPbStride * 2, pk[e]);
-                lds_write_u16_hi(pb1 + e * kPbStride * 2, pk[e]);
+                lds_write_u16(pb0 + e * kPbJStride * 2, pk[e]);
+                lds_write_u16_hi(pb1 + e * kPbJStride * 2, pk[e]);
             }
             if (lane < kStepRows) {
                 const bool in_slab = kStepRows * k + lane < slab_rows;
@@ -493,47 +498,53 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
 
     char *d_cur = reinterpret_cast<char *>(dx + row0 * K + kw);
     const char *a_cur = reinterpret_cast<const char *>(addend + row0 * K + kw);
+    // The ready count of a step's slot is read one step early, so that its
+    // round trip is off the step's critical path.
+    uint32_t ready_seen = lds_read_u32(ready_addr);
     for (int j = 0; j < nsteps; ++j) {
         const int rows_left = slab_rows - kStepRows * j;
-        // Wait for this step's X.  Each step issues, in this order: [4 addend
-        // loads] 4 X DMA (for step j + 1), 4 dX stores; the X of step j was
-        // requested in step j - 1 with only that step's 4 stores after it,
-        // so vmcnt(4) covers it.  Step 0 waits for everything.  Steps past
-        // the slab end are still requested (they read zeros; their stores
-        // fall outside the range), which keeps every step's count identical.
+        const int slot = j % kSlots;
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ready_seen)::"memory");
+        const uint32_t want = static_cast<uint32_t>(j / kSlots + 1);
+        if (__builtin_amdgcn_readfirstlane(ready_seen) < want)
+            lds_wait_at_least(ready_addr + 4 * slot, want);
+        const StepP &cur = pop[slot];
+        // The P operands of this step are requested first: the RMS
+        // coefficients of rows 4g..4g+3, the dX P operands (token c16, part
+        // p, j = 16b + 4g .. +3) and the dW P operands (part p, j = 16b +
+        // c16, rows 4g .. 4g+3; entries j >= 24 are zero).
+        f32x4 cc = lds_read_b128(lds_addr(cur.c + 4 * g));
+        u32x4 pa[2][2];  // [part][block]
+        u32x4 pbv[2];    // [block]: part 0 in .xy, part 1 in .zw
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                pa[p][b] = lds_read_u128(
+                    lds_addr(cur.pa + c16 * kPaStride + p * kJPad + 16 * b + 4 * g));
+            pbv[b] = lds_read_u128(lds_addr(cur.pb + (16 * b + c16) * kPbJStride + 8 * g));
+        }
+        // Then wait for this step's X and read it (4 rows).  Each step
+        // issues, in this order: [4 addend loads] 4 X DMA (for step j + 1),
+        // 4 dX stores; the X of step j was requested in step j - 1 with only
+        // that step's 4 stores after it, so vmcnt(4) covers it.  Step 0 waits
+        // for everything.  Steps past the slab end are still requested (they
+        // read zeros; their stores fall outside the range), which keeps every
+        // step's count identical.
         if (j == 0)
             wait_vmcnt<0>();
         else
             wait_vmcnt<4>();
-        const int slot = j % kSlots;
-        lds_wait_at_least(ready_addr + 4 * slot, static_cast<uint32_t>(j / kSlots + 1));
-        const StepP &cur = pop[slot];
         const uint32_t xa = ring_base + static_cast<uint32_t>((((j & 1) * 4) * kWave + lane) * 16);
-        // Every LDS operand of this step in one batch: X (4 rows), the RMS
-        // coefficients of rows 4g..4g+3, the dX P operands (token c16, part
-        // p, j = 16b + 4g .. +3) and the dW P operands (part p, j = 16b +
-        // c16, rows 4g .. 4g+3; entries j >= 24 are zero).
         f32x4 xc[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) xc[rr] = lds_read_b128(xa + rr * kWave * 16);
-        f32x4 cc = lds_read_b128(lds_addr(cur.c + 4 * g));
-        u32x4 pa[2][2];  // [part][block]
-        u32x2 pbv[2][2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                pa[p][b] = lds_read_u128(
-                    lds_addr(cur.pa + c16 * kPaStride + p * kJPad + 16 * b + 4 * g));
-                pbv[p][b] = lds_read_u64(
-                    lds_addr(cur.pb + (p * kJPad + 16 * b + c16) * kPbStride + 4 * g));
-            }
         // The wait names every register the reads above return, so no use
         // of them can be scheduled before the data has arrived.
         asm volatile("s_waitcnt lgkmcnt(0)"
                      : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
                        "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]), "+v"(pa[1][1]),
-                       "+v"(pbv[0][0]), "+v"(pbv[0][1]), "+v"(pbv[1][0]), "+v"(pbv[1][1])::"memory");
+                       "+v"(pbv[0]), "+v"(pbv[1])::"memory");
         lds_signal(consumed_addr + 4 * slot, lane);
         uint2 av[4];
         const int d_range = range_elems(rows_left) * 2;
@@ -557,7 +568,8 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         for (int p = 0; p < 2; ++p)
 #pragma unroll
             for (int b = 0; b < 2; ++b)
-                pb[p][b] = u32x4{pbv[p][b].x, pbv[p][b].y, pbv[p][b].x, pbv[p][b].y};
+                pb[p][b] = p == 0 ? u32x4{pbv[b].x, pbv[b].y, pbv[b].x, pbv[b].y}
+                                  : u32x4{pbv[b].z, pbv[b].w, pbv[b].z, pbv[b].w};
 
         uint32_t packed[4][2];  // dX of row 4g + r, columns (0,1) and (2,3)
 #pragma unroll
@@ -606,7 +618,9 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[rr][0], packed[rr][1]}, drs, doff[rr],
                                                   0, MHCPB_DX_AUX);
         d_cur += kStepRows * row_bytes_d;
+        ready_seen = lds_read_u32(ready_addr + 4 * ((j + 1) % kSlots));
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ready_seen)::"memory");
     // Drain the X DMA still in flight (the step past the slab end) before
     // the workgroup's LDS can be released.
     wait_vmcnt<0>();
@@ -630,21 +644,28 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
 }
 
 // dW[i] = (((ws[0][i] + ws[1][i]) + ws[2][i]) + ...), four elements per thread.
+// The slabs are loaded eight at a time before they are added (in order), so
+// the loads overlap.
+constexpr int kReduceBatch = 8;
 __global__ __launch_bounds__(256) void reduce_slabs(const float *__restrict__ ws,
                                                     float *__restrict__ dw, int S,
                                                     int64_t n4) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= n4) return;
-    const float4 *src = reinterpret_cast<const float4 *>(ws);
-    float4 a = src[i];
-    for (int s = 1; s < S; ++s) {
-        const float4 b = src[static_cast<int64_t>(s) * n4 + i];
-        a.x += b.x;
-        a.y += b.y;
-        a.z += b.z;
-        a.w += b.w;
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(ws) + i;
+    f32x4 a = __builtin_nontemporal_load(src);
+    for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
+        f32x4 b[kReduceBatch];
+        // Past the last slab the addend is -0, which leaves every sum as it
+        // is (x + -0 == x, signed zeros included).
+#pragma unroll
+        for (int u = 0; u < kReduceBatch; ++u)
+            b[u] = (s0 + u < S) ? __builtin_nontemporal_load(src + static_cast<int64_t>(s0 + u) * n4)
+                                : f32x4{-0.f, -0.f, -0.f, -0.f};
+#pragma unroll
+        for (int u = 0; u < kReduceBatch; ++u) a += b[u];
     }
-    reinterpret_cast<float4 *>(dw)[i] = a;
+    reinterpret_cast<f32x4 *>(dw)[i] = a;
 }
 
 template <int NW>
