@@ -345,55 +345,6 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                                                  (MHCPB_LDS void *)d.r, 4,
                                                  static_cast<uint32_t>(lane * 4), 0, 0, 0);
     };
-    if (producer) {
-#pragma unroll
-        for (int k = 0; k < kRawAhead; ++k) issue_raw(k);
-    }
-
-    // ---- compute waves: X ring, W in registers.
-    const int64_t kw = static_cast<int64_t>(blockIdx.x) * (NW * 64) + (producer ? 0 : wave) * 64;
-    const int kwi = static_cast<int>(kw);  // kw < K + NW * 64
-    const int64_t col = kw + 4 * c16;      // first of this lane's 4 columns
-    const bool active = !producer && col < K;
-    // A step is addressed through one buffer resource per tensor, based at
-    // row t0 and column kw, whose range ends at the slab end or 16 rows on,
-    // whichever comes first; lane offsets (row 4g + r, columns 4c..4c+3) go
-    // in the per-lane offset, which the hardware range check covers (the
-    // scalar offset, which is not checked, stays zero).  An element of a
-    // slab row lies in the range because K and the lane's column are
-    // multiples of 4; a row past the slab end lies outside it.  Inactive
-    // columns get an offset outside every range, so their loads read zeros
-    // and their stores are dropped.
-    uint32_t xoff[4], doff[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        xoff[rr] = active ? static_cast<uint32_t>(((4 * g + rr) * K + 4 * c16) * 4) : kOutOfRange;
-        doff[rr] = active ? static_cast<uint32_t>(((4 * g + rr) * K + 4 * c16) * 2) : kOutOfRange;
-    }
-    // Elements of the range of a step resource (times the element size).
-    auto range_elems = [&](int rows_left) {
-        const int rl = rows_left < 0 ? 0 : (rows_left > kStepRows ? kStepRows : rows_left);
-        const int n = rl * ki - kwi;
-        return __builtin_amdgcn_readfirstlane(n > 0 ? n : 0);
-    };
-    const int64_t row_bytes_x = K * 4;  // one row of X
-    const int64_t row_bytes_d = K * 2;  // one row of dX or the addend
-    const int xw = producer ? 0 : wave;
-    const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&xring[xw][0][0][0]));
-    // xs points at row 0, column kw of a step; rows_left counts the slab rows
-    // from there on.
-    auto issue_x = [&](const char *xs, int rows_left, int stage) {
-        const __amdgpu_buffer_rsrc_t xrs = make_rsrc32(xs, range_elems(rows_left) * 4);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xrs, (MHCPB_LDS void *)(&xring[xw][stage][rr][0]), 16, xoff[rr], 0, 0, MHCPB_X_AUX);
-    };
-    const char *x_next = reinterpret_cast<const char *>(x + row0 * K + kw);
-    if (!producer) {
-        issue_x(x_next, slab_rows, 0);
-        x_next += kStepRows * row_bytes_x;
-    }
 
     // The j = 24..31 entries of every operand slot are zero padding; the
     // counters start at zero.
@@ -414,9 +365,11 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         lds_write_u32(ready_addr + 4 * tid, 0u);
         lds_write_u32(consumed_addr + 4 * tid, 0u);
     }
-    lds_barrier();
 
     if (producer) {
+#pragma unroll
+        for (int k = 0; k < kRawAhead; ++k) issue_raw(k);
+        lds_barrier();
         // Lane = row * 4 + q converts j = 6q .. 6q + 5 of one row of P into
         // both operand layouts; lanes 0..15 also compute the RMS coefficient
         // grad_r / (r K) of row lane in FP32 (zero past the slab end).
@@ -467,23 +420,78 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         return;
     }
 
+    // ---- compute waves: X ring, W in registers.
+    const int64_t kw = static_cast<int64_t>(blockIdx.x) * (NW * 64) + wave * 64;
+    const int kwi = static_cast<int>(kw);  // kw < K + NW * 64
+    const int64_t col = kw + 4 * c16;      // first of this lane's 4 columns
+    const bool active = col < K;
+    // A step is addressed through one buffer resource per tensor, based at
+    // row t0 and column kw, whose range ends at the slab end or 16 rows on,
+    // whichever comes first; lane offsets (row 4g + r, columns 4c..4c+3) go
+    // in the per-lane offset, which the hardware range check covers (the
+    // scalar offset, which is not checked, stays zero).  An element of a
+    // slab row lies in the range because K and the lane's column are
+    // multiples of 4; a row past the slab end lies outside it.  Inactive
+    // columns get an offset outside every range, so their loads read zeros
+    // and their stores are dropped.
+    uint32_t xoff[4], doff[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        xoff[rr] = active ? static_cast<uint32_t>(((4 * g + rr) * K + 4 * c16) * 4) : kOutOfRange;
+        doff[rr] = active ? static_cast<uint32_t>(((4 * g + rr) * K + 4 * c16) * 2) : kOutOfRange;
+    }
+    // Elements of the range of a step resource (times the element size).
+    auto range_elems = [&](int rows_left) {
+        const int rl = rows_left < 0 ? 0 : (rows_left > kStepRows ? kStepRows : rows_left);
+        const int n = rl * ki - kwi;
+        return __builtin_amdgcn_readfirstlane(n > 0 ? n : 0);
+    };
+    const int64_t row_bytes_x = K * 4;  // one row of X
+    const int64_t row_bytes_d = K * 2;  // one row of dX or the addend
+    const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&xring[wave][0][0][0]));
+    // xs points at row 0, column kw of a step; rows_left counts the slab rows
+    // from there on.
+    auto issue_x = [&](const char *xs, int rows_left, int stage) {
+        const __amdgpu_buffer_rsrc_t xrs = make_rsrc32(xs, range_elems(rows_left) * 4);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xrs, (MHCPB_LDS void *)(&xring[wave][stage][rr][0]), 16, xoff[rr], 0, 0, MHCPB_X_AUX);
+    };
+    // W of this lane's columns (for the dX product): loaded first, then the X
+    // of steps 0 and 1 (both ring stages are free at the start), so that the
+    // wait for W below does not wait for X, and two steps stream in while the
+    // prologue runs.
+    float4 wraw[2][4];  // [j block][e]: W[16 b + 4 g + e][col .. col + 3]
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int jj = 16 * b + 4 * g + e;
+            wraw[b][e] = (active && jj < kProjCols) ? *reinterpret_cast<const float4 *>(w + jj * K + col)
+                                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    compiler_fence();
+    const char *x_next = reinterpret_cast<const char *>(x + row0 * K + kw);
+    issue_x(x_next, slab_rows, 0);
+    issue_x(x_next + kStepRows * row_bytes_x, slab_rows - kStepRows, 1);
+    x_next += 2 * kStepRows * row_bytes_x;
+    compiler_fence();
+    // Padding and counters visible (the producer passes the same barrier).
+    lds_barrier();
+
+
+
     // W side of the dX product: for column variant i and j block b the lane
     // holds the packed (hi | lo << 16) TF32 split of W[j][col + i] for
     // j = 16b + 4g .. 16b + 4g + 3 (zero for j >= 24).
     u32x4 bw[4][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-        float wv[4][4];  // [e][i]
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = 16 * b + 4 * g + e;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (active && j < kProjCols) v = *reinterpret_cast<const float4 *>(w + j * K + col);
-            wv[e][0] = v.x;
-            wv[e][1] = v.y;
-            wv[e][2] = v.z;
-            wv[e][3] = v.w;
-        }
+        const float wv[4][4] = {{wraw[b][0].x, wraw[b][0].y, wraw[b][0].z, wraw[b][0].w},
+                                {wraw[b][1].x, wraw[b][1].y, wraw[b][1].z, wraw[b][1].w},
+                                {wraw[b][2].x, wraw[b][2].y, wraw[b][2].z, wraw[b][2].w},
+                                {wraw[b][3].x, wraw[b][3].y, wraw[b][3].z, wraw[b][3].w}};  // [e][i]
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             bw[i][b] = u32x4{tf32_split_packed(wv[0][i]), tf32_split_packed(wv[1][i]),
@@ -524,17 +532,16 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                     lds_addr(cur.pa + c16 * kPaStride + p * kJPad + 16 * b + 4 * g));
             pbv[b] = lds_read_u128(lds_addr(cur.pb + (16 * b + c16) * kPbJStride + 8 * g));
         }
-        // Then wait for this step's X and read it (4 rows).  Each step
+        // Then wait for this step's X and read it (4 rows).  Step j >= 1
         // issues, in this order: [4 addend loads] 4 X DMA (for step j + 1),
-        // 4 dX stores; the X of step j was requested in step j - 1 with only
-        // that step's 4 stores after it, so vmcnt(4) covers it.  Step 0 waits
-        // for everything.  Steps past the slab end are still requested (they
-        // read zeros; their stores fall outside the range), which keeps every
-        // step's count identical.
-        if (j == 0)
-            wait_vmcnt<0>();
-        else
-            wait_vmcnt<4>();
+        // 4 dX stores; step 0 issues no X (the prologue requested steps 0 and
+        // 1, after the W loads).  So only 4 VMEM instructions can follow the
+        // X of step j that are not yet known complete (the X of step 1 for
+        // step 0, the previous step's stores otherwise): vmcnt(4) covers it
+        // (with the addend loads, the wait is only stricter).  Steps past the
+        // slab end are still requested (they read zeros; their stores fall
+        // outside the range), which keeps every step's count identical.
+        wait_vmcnt<4>();
         const uint32_t xa = ring_base + static_cast<uint32_t>((((j & 1) * 4) * kWave + lane) * 16);
         f32x4 xc[4];
 #pragma unroll
@@ -558,8 +565,10 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
             a_cur += kStepRows * row_bytes_d;
         }
         compiler_fence();
-        issue_x(x_next, rows_left - kStepRows, (j + 1) & 1);
-        x_next += kStepRows * row_bytes_x;
+        if (j > 0) {
+            issue_x(x_next, rows_left - kStepRows, (j + 1) & 1);
+            x_next += kStepRows * row_bytes_x;
+        }
         compiler_fence();
 
         const float ce[4] = {cc[0], cc[1], cc[2], cc[3]};
