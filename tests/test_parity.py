@@ -123,3 +123,25 @@ def test_full_size_sampled(name):
     # every dX and dW element is finite (the poison is gone everywhere)
     assert bool(torch.isfinite(dx.float()).all().item())
     assert bool(torch.isfinite(dw).all().item())
+
+
+def test_max_hidden_sampled():
+    """The widest supported row (hidden = 2^20, K = 4,194,304 columns) over 40
+    tokens (three steps, the last one ragged): offsets and ranges at their
+    largest.  Sampled dX rows (every column) and dW columns near both ends."""
+    wl = workloads.custom(40, 4, 1 << 20, seed=77, rescale_rows=True)
+    print(f"T={wl.T} K={wl.K}", flush=True)
+    inp = workloads.make(wl, "cuda")
+    dx, dw, ws, plan = gh.run(inp)
+    S = mhcpb_plan_split_count(plan.handle)
+    L = -(-wl.T // S)
+    rows = [0, 15, 16, 31, 32, 39]
+    h = gh.host_rows(inp, rows)
+    dx_rows = gh.bf16_bits_np(dx.index_select(0, torch.as_tensor(rows, device="cuda")))
+    _check_dx(dx_rows, h, wl.K, "max hidden")
+    K = wl.K
+    cols = sorted({0, 1, 2, 3, 319, 320, K // 2, K - 321, K - 320, K - 65, K - 64, K - 4,
+                   K - 3, K - 2, K - 1})
+    _check_dw(gh.host(dw)[:, cols], gh.host_cols(inp, cols), L, S, "max hidden")
+    assert bool(torch.isfinite(dx.float()).all().item())
+    assert bool(torch.isfinite(dw).all().item())
