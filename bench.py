@@ -185,8 +185,9 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     us_per_call = e0.elapsed_time(e1) * 1e3 / args.steps
 
-    # per-kernel durations: the same calls, with HIP events the library records
-    # on the launch stream before kernel 1, between the kernels and after kernel 2
+    # per-kernel durations: the same calls, with HIP events the library attaches
+    # to the two dispatches on the launch stream (start and end of kernel 1, end
+    # of kernel 2)
     hev = HipEvents()
     n = args.steps
     evs = [(hev.create(), hev.create(), hev.create()) for _ in range(n)]

@@ -117,10 +117,13 @@ mhcpb_status_t mhcpb_execute(mhcpb_plan_t plan, const float *x, const float *w,
                              size_t workspace_size, hipStream_t stream);
 
 /*
- * Same as mhcpb_execute, and records `before_k1`, `after_k1` and `after_k2`
- * on `stream` around the two kernels (any of them may be NULL), so a caller
- * can time each kernel with hipEventElapsedTime.  The events are created and
- * owned by the caller.
+ * Same as mhcpb_execute, and attaches caller events to the kernel launches
+ * (any of them may be NULL): `before_k1` takes the start time of kernel 1,
+ * `after_k1` its end time, `after_k2` the end time of kernel 2.  The times
+ * come from the dispatches themselves (hipExtLaunchKernel), so no marker is
+ * inserted between the kernels: hipEventElapsedTime(before_k1, after_k1) is
+ * kernel 1's execution time and (after_k1, after_k2) kernel 2's plus the gap
+ * between them.  The events are created and owned by the caller.
  */
 mhcpb_status_t mhcpb_execute_with_events(
     mhcpb_plan_t plan, const float *x, const float *w, const float *grad_proj,

@@ -43,10 +43,13 @@ struct Args {
     float *ws;
 };
 
-// Kernel 1: one pass over X; writes dX and the S partial dW slabs.
-hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream);
-// Kernel 2: dW = sum of the S slabs in ascending order.
-hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream);
+// Kernel 1: one pass over X; writes dX and the S partial dW slabs.  The
+// optional events take the start and end times of the dispatch.
+hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop);
+// Kernel 2: dW = sum of the S slabs in ascending order; the optional event
+// takes the end time of the dispatch.
+hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop);
 
 }  // namespace mhcpb
 

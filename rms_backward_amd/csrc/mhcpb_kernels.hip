@@ -25,6 +25,7 @@
 // a ring of D steps per wave, so prefetching costs no registers; rows past
 // the slab end fall outside the buffer range and arrive as zeros.  The P rows
 // of each step arrive the same way a few steps ahead.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -678,16 +679,19 @@ __global__ __launch_bounds__(256) void reduce_slabs(const float *__restrict__ ws
 }
 
 template <int NW>
-hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream) {
+hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t start,
+                               hipEvent_t stop) {
     constexpr int cols = NW * 64;
     const dim3 grid(static_cast<unsigned>((p.K + cols - 1) / cols), static_cast<unsigned>(p.S));
     const dim3 block((NW + 1) * kWave);
     if (a.addend)
-        hipLaunchKernelGGL((projection_kernel<NW, true>), grid, block, 0, stream, a.x, a.w,
-                           a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L);
+        hipExtLaunchKernelGGL((projection_kernel<NW, true>), grid, block, 0, stream, start, stop, 0,
+                              a.x, a.w, a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K,
+                              p.L);
     else
-        hipLaunchKernelGGL((projection_kernel<NW, false>), grid, block, 0, stream, a.x, a.w,
-                           a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L);
+        hipExtLaunchKernelGGL((projection_kernel<NW, false>), grid, block, 0, stream, start, stop, 0,
+                              a.x, a.w, a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K,
+                              p.L);
     return hipGetLastError();
 }
 
@@ -698,14 +702,16 @@ hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream)
 // Five compute waves and the producer make two workgroups per CU exactly
 // three waves per SIMD; at K = 20480 with 8 splits the grid is one full round
 // of two workgroups per CU on 256 CUs.
-hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream) {
-    return launch_projection_t<5>(p, a, stream);
+hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t start,
+                             hipEvent_t stop) {
+    return launch_projection_t<5>(p, a, stream, start, stop);
 }
 
-hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream) {
+hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop) {
     const int64_t n4 = kProjCols * p.K / 4;
     const unsigned blocks = static_cast<unsigned>((n4 + 255) / 256);
-    hipLaunchKernelGGL(reduce_slabs, dim3(blocks), dim3(256), 0, stream, a.ws, a.dw, p.S, n4);
+    hipExtLaunchKernelGGL(reduce_slabs, dim3(blocks), dim3(256), 0, stream, nullptr, stop, 0, a.ws,
+                          a.dw, p.S, n4);
     return hipGetLastError();
 }
 

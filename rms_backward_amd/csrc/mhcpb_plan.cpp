@@ -77,15 +77,9 @@ mhcpb_status_t run(mhcpb_plan_t plan, const float *x, const float *w,
     if (st != MHCPB_SUCCESS)
         return st;
     mhcpb::Args a{x, w, grad_proj, grad_r, r, dx, dw, addend, static_cast<float *>(ws)};
-    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess)
+    if (mhcpb::launch_projection(p, a, stream, ev0, ev1) != hipSuccess)
         return MHCPB_ERROR_LAUNCH;
-    if (mhcpb::launch_projection(p, a, stream) != hipSuccess)
-        return MHCPB_ERROR_LAUNCH;
-    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess)
-        return MHCPB_ERROR_LAUNCH;
-    if (mhcpb::launch_reduce(p, a, stream) != hipSuccess)
-        return MHCPB_ERROR_LAUNCH;
-    if (ev2 && hipEventRecord(ev2, stream) != hipSuccess)
+    if (mhcpb::launch_reduce(p, a, stream, ev2) != hipSuccess)
         return MHCPB_ERROR_LAUNCH;
     return MHCPB_SUCCESS;
 }
