@@ -22,9 +22,9 @@
 // column group.  No operand needs a per-step shuffle.
 //
 // X is streamed from HBM straight into LDS with buffer_load_dwordx4 ... lds,
-// a ring of D steps per wave, so prefetching costs no registers; rows past
-// the slab end fall outside the buffer range and arrive as zeros.  The P rows
-// of each step arrive the same way a few steps ahead.
+// a two-step ring per wave, so prefetching costs no registers; rows past the
+// slab end fall outside the buffer range and arrive as zeros.  The P rows of
+// each step arrive the same way a few steps ahead.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -86,8 +86,8 @@ __device__ __forceinline__ void tf32_split(float v, uint32_t &hi_bits, float &lo
     lo = __uint_as_float(t) - __uint_as_float(h);
 }
 
-// The same split for the small operands (P, W) packed as hi | lo << 16, with
-// non-finite inputs kept non-finite in the high part and a zero low part.
+// The same split for W, packed as hi | lo << 16, with non-finite inputs kept
+// non-finite in the high part and a zero low part.
 __device__ __forceinline__ uint32_t tf32_split_packed(float v) {
     const uint32_t u = __float_as_uint(v);
     uint32_t hb;
@@ -98,7 +98,7 @@ __device__ __forceinline__ uint32_t tf32_split_packed(float v) {
     return ((u & 0x7F800000u) == 0x7F800000u) ? quiet : finite;
 }
 
-// The split of a P value for the staging wave: like tf32_split_packed for
+// The split of a P value for the producer wave: like tf32_split_packed for
 // finite values; a NaN is first replaced by the canonical quiet NaN (so the
 // rounding cannot carry it out of the exponent), and an infinity keeps an
 // infinite high part (its low part is then NaN).  Either way every product
@@ -166,8 +166,9 @@ __device__ __forceinline__ u32x2 lds_read_u64(uint32_t addr) {
     return v;
 }
 
-// LDS writes of the P staging, equally hidden from the compiler's LDS-DMA
-// ordering (they never touch the X ring); completed by lds_barrier().
+// LDS writes of the operand staging and the counters, equally hidden from the
+// compiler's LDS-DMA ordering (they never touch the X ring); a wave waits for
+// them (lgkmcnt) before it passes a barrier or signals a counter.
 __device__ __forceinline__ void lds_write_u32(uint32_t addr, uint32_t v) {
     asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
@@ -481,8 +482,6 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     // Padding and counters visible (the producer passes the same barrier).
     lds_barrier();
 
-
-
     // W side of the dX product: for column variant i and j block b the lane
     // holds the packed (hi | lo << 16) TF32 split of W[j][col + i] for
     // j = 16b + 4g .. 16b + 4g + 3 (zero for j >= 24).
@@ -536,11 +535,11 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         // Then wait for this step's X and read it (4 rows).  Step j >= 1
         // issues, in this order: [4 addend loads] 4 X DMA (for step j + 1),
         // 4 dX stores; step 0 issues no X (the prologue requested steps 0 and
-        // 1, after the W loads).  So only 4 VMEM instructions can follow the
-        // X of step j that are not yet known complete (the X of step 1 for
-        // step 0, the previous step's stores otherwise): vmcnt(4) covers it
-        // (with the addend loads, the wait is only stricter).  Steps past the
-        // slab end are still requested (they read zeros; their stores fall
+        // 1, after the W loads).  So after the X of step j come at most the 4
+        // stores of step j - 1 (the X of step 1 for step 0): vmcnt(4) covers
+        // it.  For step 1 with the addend, step 0's addend loads come after
+        // the X of step 1 as well, and the wait is only stricter.  Steps past
+        // the slab end are still requested (they read zeros; their stores fall
         // outside the range), which keeps every step's count identical.
         wait_vmcnt<4>();
         const uint32_t xa = ring_base + static_cast<uint32_t>((((j & 1) * 4) * kWave + lane) * 16);
