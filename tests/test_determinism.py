@@ -42,3 +42,31 @@ def test_identical_across_separate_plans_and_streams():
     s.synchronize()
     assert torch.equal(dw1.view(torch.int32), dw0.view(torch.int32))
     assert torch.equal(dx1.view(torch.int16), dx0.view(torch.int16))
+
+
+@pytest.mark.parametrize("addend", [False, True])
+def test_execute_with_events_matches_execute(addend):
+    """The timing entry point launches the same kernels: identical bits, and
+    the events it attaches to the two dispatches give positive durations."""
+    from bench import HipEvents
+    from rms_backward_amd import mhcpb_execute_with_events
+    wl = workloads.custom(1100, 4, 1280, seed=5, addend=addend)
+    inp = workloads.make(wl, "cuda")
+    dx0, dw0, _, plan = gh.run(inp)
+    dx0, dw0 = dx0.clone(), dw0.clone()
+    dx, dw, ws = gh.alloc_outputs(wl.T, wl.K, plan, "cuda")
+    hev = HipEvents()
+    evs = [hev.create() for _ in range(3)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    mhcpb_execute_with_events(plan.handle, inp["x"], inp["w"], inp["grad_proj"], inp["grad_r"],
+                              inp["r"], dx, dw, inp.get("addend"), ws, ws.numel(),
+                              stream.cuda_stream, *evs)
+    torch.cuda.synchronize()
+    k1 = hev.elapsed_ms(evs[0], evs[1])
+    k2 = hev.elapsed_ms(evs[1], evs[2])
+    for e in evs:
+        hev.destroy(e)
+    assert torch.equal(dw.view(torch.int32), dw0.view(torch.int32))
+    assert torch.equal(dx.view(torch.int16), dx0.view(torch.int16))
+    assert 0.0 < k1 < 1e3 and 0.0 < k2 < 1e3, (k1, k2)
