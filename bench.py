@@ -141,7 +141,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="train")
-    ap.add_argument("--cpu-rows", type=int, default=512,
+    ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows of the workload the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
