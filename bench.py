@@ -237,6 +237,7 @@ def main(argv=None):
                          f"dW FP32" + (", BF16 addend" if wl.addend else "")),
             "T": T, "K": K, "splits": S,
             "bytes_per_call": call_bytes,
+            "bytes_per_call_without_partials": call_bytes - 2 * S * 24 * K * 4,
             "k1_us": round(k1_us, 2), "k2_us": round(k2_us, 2),
             "timed_wall_s": round(wall, 4),
         },

@@ -677,6 +677,17 @@ __global__ __launch_bounds__(256) void reduce_slabs(const float *__restrict__ ws
     reinterpret_cast<f32x4 *>(dw)[i] = a;
 }
 
+// A launch with the given events attached to the dispatch (start and end
+// times), or a plain launch when both are null.
+template <typename... KArgs, typename... Args>
+void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start,
+            hipEvent_t stop, Args... args) {
+    if (start || stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+}
+
 template <int NW>
 hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop) {
@@ -684,13 +695,11 @@ hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream,
     const dim3 grid(static_cast<unsigned>((p.K + cols - 1) / cols), static_cast<unsigned>(p.S));
     const dim3 block((NW + 1) * kWave);
     if (a.addend)
-        hipExtLaunchKernelGGL((projection_kernel<NW, true>), grid, block, 0, stream, start, stop, 0,
-                              a.x, a.w, a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K,
-                              p.L);
+        launch(projection_kernel<NW, true>, grid, block, stream, start, stop, a.x, a.w, a.grad_proj,
+               a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L);
     else
-        hipExtLaunchKernelGGL((projection_kernel<NW, false>), grid, block, 0, stream, start, stop, 0,
-                              a.x, a.w, a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K,
-                              p.L);
+        launch(projection_kernel<NW, false>, grid, block, stream, start, stop, a.x, a.w,
+               a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L);
     return hipGetLastError();
 }
 
@@ -709,8 +718,7 @@ hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream, h
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop) {
     const int64_t n4 = kProjCols * p.K / 4;
     const unsigned blocks = static_cast<unsigned>((n4 + 255) / 256);
-    hipExtLaunchKernelGGL(reduce_slabs, dim3(blocks), dim3(256), 0, stream, nullptr, stop, 0, a.ws,
-                          a.dw, p.S, n4);
+    launch(reduce_slabs, dim3(blocks), dim3(256), stream, nullptr, stop, a.ws, a.dw, p.S, n4);
     return hipGetLastError();
 }
 

@@ -70,3 +70,4 @@ def test_execute_with_events_matches_execute(addend):
     assert torch.equal(dw.view(torch.int32), dw0.view(torch.int32))
     assert torch.equal(dx.view(torch.int16), dx0.view(torch.int16))
     assert 0.0 < k1 < 1e3 and 0.0 < k2 < 1e3, (k1, k2)
+
