@@ -124,6 +124,86 @@ def cpu_baseline(inp, rows: int, T: int, K: int, S: int, addend: bool):
     }
 
 
+def split_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
+    """Algorithmic bytes of (mhcpb_execute_dx, mhcpb_execute_dw) calls."""
+    dx = T * K * 4 + T * K * 2 + (T * K * 2 if addend else 0) + 24 * K * 4 + 24 * T * 4 + 2 * T * 4
+    dw = T * K * 4 + 24 * T * 4 + 2 * S * 24 * K * 4 + 24 * K * 4
+    return dx, dw
+
+
+def run_split(args, wl, inp, plan, S, dx, dw, ws) -> dict:
+    """The split form: per step, the dX-only call then the dW-only call."""
+    import torch
+    from rms_backward_amd import mhcpb_execute_dw, mhcpb_execute_dx
+    T, K = wl.T, wl.K
+    stream = torch.cuda.current_stream()
+    h = plan.handle
+    call_dx = lambda: mhcpb_execute_dx(h, inp["x"], inp["w"], inp["grad_proj"], inp["grad_r"],
+                                       inp["r"], dx, inp.get("addend"), stream.cuda_stream)
+    call_dw = lambda: mhcpb_execute_dw(h, inp["x"], inp["grad_proj"], dw, ws, ws.numel(),
+                                       stream.cuda_stream)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    for _ in range(args.warmup):
+        call_dx()
+        call_dw()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    us_per_step = timed(lambda: (call_dx(), call_dw()), args.steps)
+    wall = time.perf_counter() - t0
+    dx_us = timed(call_dx, args.steps)
+    dw_us = timed(call_dw, args.steps)
+    dx_bytes, dw_bytes = split_bytes(T, K, S, wl.addend)
+    gbps = (dx_bytes + dw_bytes) / (us_per_step * 1e-6) / 1e9
+    dx_gbps = dx_bytes / (dx_us * 1e-6) / 1e9
+    return {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_step / 1e3, 6),
+        "us_per_call": round(us_per_step, 2),
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "tf32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name}: T={T} tokens, {wl.streams} streams x hidden "
+                         f"{wl.hidden} (K={K}); split form (dX call, then dW call)"
+                         + (", BF16 addend" if wl.addend else "")),
+            "form": "split", "T": T, "K": K, "splits": S,
+            "bytes_per_step": dx_bytes + dw_bytes,
+            "dx_call_bytes": dx_bytes, "dw_call_bytes": dw_bytes,
+            "dx_call_us": round(dx_us, 2), "dw_call_us": round(dw_us, 2),
+            "timed_wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(dx_gbps, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(dx_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+            "kernel": "projection, dX-only form (one kernel per call, timed over the calls)",
+            "bytes_per_launch": dx_bytes,
+        },
+    }
+
+
 def run_copy_calibration(nbytes: int, reps: int):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -144,6 +224,9 @@ def main(argv=None):
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows of the workload the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--form", choices=("fused", "split"), default="fused",
+                    help="fused: mhcpb_execute per step; split: mhcpb_execute_dx then "
+                         "mhcpb_execute_dw per step (X read twice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter scaling)")
     args = ap.parse_args(argv)
@@ -172,6 +255,15 @@ def main(argv=None):
     plan = Plan(T, wl.streams, wl.hidden)
     S = mhcpb_plan_split_count(plan.handle)
     dx, dw, ws = gh.alloc_outputs(T, K, plan, "cuda", poison=True)
+    if args.form == "split":
+        out = run_split(args, wl, inp, plan, S, dx, dw, ws)
+        if not args.no_cpu_baseline:
+            print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+            out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, T, K, S, wl.addend)
+        else:
+            out["cpu_baseline"] = None
+        print(json.dumps(out), flush=True)
+        return 0
     call = lambda: plan.execute(inp["x"], inp["w"], inp["grad_proj"], inp["grad_r"], inp["r"],
                                 dx, dw, ws, inp.get("addend"))
     for _ in range(args.warmup):

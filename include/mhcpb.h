@@ -132,6 +132,31 @@ mhcpb_status_t mhcpb_execute_with_events(
     hipStream_t stream, hipEvent_t before_k1, hipEvent_t after_k1,
     hipEvent_t after_k2);
 
+/*
+ * The split backward ("FP8 weight cache, split backward, fused mHC stream
+ * gradient" on the prime-kernels page: the data gradient first, the weight
+ * gradients after, so a caller can send dX on before dW is computed).  Each
+ * form reads X once, so the pair reads it twice; each output has exactly the
+ * bits mhcpb_execute gives it.
+ *
+ * mhcpb_execute_dx: one kernel writing dX only (arguments as in
+ * mhcpb_execute; no dW, no workspace).  Required: x, w, grad_proj, grad_r, r,
+ * dx; grad_x_addend may be NULL.
+ */
+mhcpb_status_t mhcpb_execute_dx(mhcpb_plan_t plan, const float *x, const float *w,
+                                const float *grad_proj, const float *grad_r,
+                                const float *r, uint16_t *dx,
+                                const uint16_t *grad_x_addend, hipStream_t stream);
+
+/*
+ * mhcpb_execute_dw: kernel 1 writing the partial dW slabs only, then kernel 2
+ * (arguments as in mhcpb_execute).  Required: x, grad_proj, dw, a workspace
+ * of at least mhcpb_workspace_bytes(plan) bytes.
+ */
+mhcpb_status_t mhcpb_execute_dw(mhcpb_plan_t plan, const float *x, const float *grad_proj,
+                                float *dw, void *workspace, size_t workspace_size,
+                                hipStream_t stream);
+
 /* A static, human-readable name for a status code. */
 const char *mhcpb_status_string(mhcpb_status_t status);
 

@@ -39,7 +39,7 @@ MHCPB_ERROR_LAUNCH = 6
 EXPORTED = (
     "mhcpb_plan_create", "mhcpb_plan_destroy", "mhcpb_workspace_bytes",
     "mhcpb_plan_split_count", "mhcpb_execute", "mhcpb_execute_with_events",
-    "mhcpb_status_string",
+    "mhcpb_execute_dx", "mhcpb_execute_dw", "mhcpb_status_string",
 )
 
 _vp = ctypes.c_void_p
@@ -57,6 +57,10 @@ _lib.mhcpb_execute.argtypes = _EXEC_ARGS
 _lib.mhcpb_execute.restype = ctypes.c_int
 _lib.mhcpb_execute_with_events.argtypes = _EXEC_ARGS + [_vp, _vp, _vp]
 _lib.mhcpb_execute_with_events.restype = ctypes.c_int
+_lib.mhcpb_execute_dx.argtypes = [_vp] * 8 + [_vp]
+_lib.mhcpb_execute_dx.restype = ctypes.c_int
+_lib.mhcpb_execute_dw.argtypes = [_vp] * 5 + [ctypes.c_size_t, _vp]
+_lib.mhcpb_execute_dw.restype = ctypes.c_int
 _lib.mhcpb_status_string.argtypes = [ctypes.c_int]
 _lib.mhcpb_status_string.restype = ctypes.c_char_p
 
@@ -133,11 +137,32 @@ def mhcpb_execute_with_events(plan, x, w, grad_proj, grad_r, r, dx, dw, grad_x_a
                               workspace, workspace_size: int, stream: int,
                               before_k1: int | None, after_k1: int | None,
                               after_k2: int | None, check: bool = True) -> int:
-    """mhcpb_execute that also records three caller-owned hipEvent_t handles."""
+    """mhcpb_execute that also attaches three caller-owned hipEvent_t handles
+    to the kernel dispatches (start and end of kernel 1, end of kernel 2)."""
     st = _lib.mhcpb_execute_with_events(
         plan, _ptr(x), _ptr(w), _ptr(grad_proj), _ptr(grad_r), _ptr(r), _ptr(dx), _ptr(dw),
         _ptr(grad_x_addend), _ptr(workspace), int(workspace_size), stream,
         before_k1, after_k1, after_k2)
     if check and st != MHCPB_SUCCESS:
         raise MhcpbError(st, "mhcpb_execute_with_events")
+    return st
+
+
+def mhcpb_execute_dx(plan, x, w, grad_proj, grad_r, r, dx, grad_x_addend, stream: int = 0,
+                     check: bool = True) -> int:
+    """The split form that writes dX only (one kernel, no workspace)."""
+    st = _lib.mhcpb_execute_dx(plan, _ptr(x), _ptr(w), _ptr(grad_proj), _ptr(grad_r), _ptr(r),
+                               _ptr(dx), _ptr(grad_x_addend), stream)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_execute_dx")
+    return st
+
+
+def mhcpb_execute_dw(plan, x, grad_proj, dw, workspace, workspace_size: int, stream: int = 0,
+                     check: bool = True) -> int:
+    """The split form that writes dW only (partial slabs, then the reduce)."""
+    st = _lib.mhcpb_execute_dw(plan, _ptr(x), _ptr(grad_proj), _ptr(dw), _ptr(workspace),
+                               int(workspace_size), stream)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_execute_dw")
     return st

@@ -43,9 +43,13 @@ struct Args {
     float *ws;
 };
 
-// Kernel 1: one pass over X; writes dX and the S partial dW slabs.  The
+// Which outputs kernel 1 produces: dX and the partial dW slabs (the fused
+// stage), dX only, or the partial slabs only.
+enum class Outputs { kBoth, kDxOnly, kDwOnly };
+
+// Kernel 1: one pass over X; writes dX and/or the S partial dW slabs.  The
 // optional events take the start and end times of the dispatch.
-hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream,
+hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop);
 // Kernel 2: dW = sum of the S slabs in ascending order; the optional event
 // takes the end time of the dispatch.

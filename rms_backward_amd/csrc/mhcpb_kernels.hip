@@ -293,9 +293,12 @@ constexpr int kRawBufs = kRawAhead + 1;
 // waits are also bounded, so a broken invariant cannot hang the GPU.  Compute
 // waves never wait for each other.
 //
+// kDX and kDW select the outputs: both (the fused stage), dX only or dW only
+// (the split forms); the arithmetic of each output is the same in every form.
+//
 // Two workgroups per CU make 12 waves (NW = 5), three per SIMD: the register
 // allocation must stay within 168 VGPRs.
-template <int NW, bool kAddend>
+template <int NW, bool kAddend, bool kDX, bool kDW>
 __global__ __launch_bounds__((NW + 1) * kWave)
 __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     const float *__restrict__ x, const float *__restrict__ w,
@@ -328,9 +331,11 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     };
 
     // ---- producer: raw P of step k into praw[k % kRawBufs], two 64-lane DMA
-    // of 16 bytes for the 16 rows of grad_proj and one of 4 bytes each for
-    // grad_r and r.  Rows past the slab end read as zeros.
+    // of 16 bytes for the 16 rows of grad_proj and, when dX is produced, one
+    // of 4 bytes each for grad_r and r (the dW-only form is given neither).
+    // Rows past the slab end read as zeros.
     const bool producer = wave == NW;
+    constexpr int kRawDma = kDX ? 4 : 2;  // DMA instructions per step
     auto issue_raw = [&](int k) {
         const int rl = step_rows(slab_rows - kStepRows * k);
         RawStep &d = praw[k % kRawBufs];
@@ -340,12 +345,14 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                                                  static_cast<uint32_t>(lane * 16), 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (MHCPB_LDS void *)(&d.p[kWave]), 16,
                                                  static_cast<uint32_t>((kWave + lane) * 16), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc32(grad_r + r0, rl * 4),
-                                                 (MHCPB_LDS void *)d.gr, 4,
-                                                 static_cast<uint32_t>(lane * 4), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc32(r + r0, rl * 4),
-                                                 (MHCPB_LDS void *)d.r, 4,
-                                                 static_cast<uint32_t>(lane * 4), 0, 0, 0);
+        if constexpr (kDX) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc32(grad_r + r0, rl * 4),
+                                                     (MHCPB_LDS void *)d.gr, 4,
+                                                     static_cast<uint32_t>(lane * 4), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc32(r + r0, rl * 4),
+                                                     (MHCPB_LDS void *)d.r, 4,
+                                                     static_cast<uint32_t>(lane * 4), 0, 0, 0);
+        }
     };
 
     // The j = 24..31 entries of every operand slot are zero padding; the
@@ -380,16 +387,19 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         for (int k = 0; k < nsteps; ++k) {
             issue_raw(k + kRawAhead);
             // The raw P of step k was requested before that of the kRawAhead
-            // steps after it, 4 DMA instructions each.
-            wait_vmcnt<4 * kRawAhead>();
+            // steps after it, kRawDma DMA instructions each.
+            wait_vmcnt<kRawDma * kRawAhead>();
             const int slot = k % kSlots;
             lds_wait_at_least(consumed_addr + 4 * slot, NW * static_cast<uint32_t>(k / kSlots));
             const RawStep &src = praw[k % kRawBufs];
             const StepP &d = pop[slot];
             const uint32_t ra = lds_addr(&src.p[0]) + static_cast<uint32_t>((prow * kProjStride + pj0) * 4);
             u32x2 v0 = lds_read_u64(ra), v1 = lds_read_u64(ra + 8), v2 = lds_read_u64(ra + 16);
-            float grv = lds_read_f32(lds_addr(&src.gr[lane]));
-            float rv = lds_read_f32(lds_addr(&src.r[lane]));
+            float grv = 0.f, rv = 1.f;
+            if constexpr (kDX) {
+                grv = lds_read_f32(lds_addr(&src.gr[lane]));
+                rv = lds_read_f32(lds_addr(&src.r[lane]));
+            }
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(grv), "+v"(rv)::"memory");
             const uint32_t vv[6] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y};
@@ -410,7 +420,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                 lds_write_u16(pb0 + e * kPbJStride * 2, pk[e]);
                 lds_write_u16_hi(pb1 + e * kPbJStride * 2, pk[e]);
             }
-            if (lane < kStepRows) {
+            if (kDX && lane < kStepRows) {
                 const bool in_slab = kStepRows * k + lane < slab_rows;
                 lds_write_u32(lds_addr(d.c + lane), __float_as_uint(in_slab ? grv / (rv * kf) : 0.f));
             }
@@ -464,15 +474,18 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     // of steps 0 and 1 (both ring stages are free at the start), so that the
     // wait for W below does not wait for X, and two steps stream in while the
     // prologue runs.
-    float4 wraw[2][4];  // [j block][e]: W[16 b + 4 g + e][col .. col + 3]
+    float4 wraw[2][4] = {};  // [j block][e]: W[16 b + 4 g + e][col .. col + 3]
+    if constexpr (kDX) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int jj = 16 * b + 4 * g + e;
-            wraw[b][e] = (active && jj < kProjCols) ? *reinterpret_cast<const float4 *>(w + jj * K + col)
-                                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+            for (int e = 0; e < 4; ++e) {
+                const int jj = 16 * b + 4 * g + e;
+                wraw[b][e] = (active && jj < kProjCols)
+                                 ? *reinterpret_cast<const float4 *>(w + jj * K + col)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+    }
     compiler_fence();
     const char *x_next = reinterpret_cast<const char *>(x + row0 * K + kw);
     issue_x(x_next, slab_rows, 0);
@@ -485,9 +498,9 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     // W side of the dX product: for column variant i and j block b the lane
     // holds the packed (hi | lo << 16) TF32 split of W[j][col + i] for
     // j = 16b + 4g .. 16b + 4g + 3 (zero for j >= 24).
-    u32x4 bw[4][2];
+    u32x4 bw[4][2] = {};
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2 && kDX; ++b) {
         const float wv[4][4] = {{wraw[b][0].x, wraw[b][0].y, wraw[b][0].z, wraw[b][0].w},
                                 {wraw[b][1].x, wraw[b][1].y, wraw[b][1].z, wraw[b][1].w},
                                 {wraw[b][2].x, wraw[b][2].y, wraw[b][2].z, wraw[b][2].w},
@@ -521,39 +534,58 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         // coefficients of rows 4g..4g+3, the dX P operands (token c16, part
         // p, j = 16b + 4g .. +3) and the dW P operands (part p, j = 16b +
         // c16, rows 4g .. 4g+3; entries j >= 24 are zero).
-        f32x4 cc = lds_read_b128(lds_addr(cur.c + 4 * g));
-        u32x4 pa[2][2];  // [part][block]
-        u32x4 pbv[2];    // [block]: part 0 in .xy, part 1 in .zw
+        f32x4 cc = {};
+        u32x4 pa[2][2] = {};  // [part][block]
+        u32x4 pbv[2] = {};    // [block]: part 0 in .xy, part 1 in .zw
+        if constexpr (kDX) cc = lds_read_b128(lds_addr(cur.c + 4 * g));
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
+            if constexpr (kDX) {
 #pragma unroll
-            for (int p = 0; p < 2; ++p)
-                pa[p][b] = lds_read_u128(
-                    lds_addr(cur.pa + c16 * kPaStride + p * kJPad + 16 * b + 4 * g));
-            pbv[b] = lds_read_u128(lds_addr(cur.pb + (16 * b + c16) * kPbJStride + 8 * g));
+                for (int p = 0; p < 2; ++p)
+                    pa[p][b] = lds_read_u128(
+                        lds_addr(cur.pa + c16 * kPaStride + p * kJPad + 16 * b + 4 * g));
+            }
+            if constexpr (kDW)
+                pbv[b] = lds_read_u128(lds_addr(cur.pb + (16 * b + c16) * kPbJStride + 8 * g));
         }
         // Then wait for this step's X and read it (4 rows).  Step j >= 1
         // issues, in this order: [4 addend loads] 4 X DMA (for step j + 1),
-        // 4 dX stores; step 0 issues no X (the prologue requested steps 0 and
-        // 1, after the W loads).  So after the X of step j come at most the 4
-        // stores of step j - 1 (the X of step 1 for step 0): vmcnt(4) covers
-        // it.  For step 1 with the addend, step 0's addend loads come after
-        // the X of step 1 as well, and the wait is only stricter.  Steps past
-        // the slab end are still requested (they read zeros; their stores fall
-        // outside the range), which keeps every step's count identical.
-        wait_vmcnt<4>();
+        // [4 dX stores]; step 0 issues no X (the prologue requested steps 0
+        // and 1, after the W loads).  So after the X of step j come at most
+        // the stores of step j - 1 (4, or none without dX), and after the X
+        // of step 0 the X of step 1: vmcnt(4), or vmcnt(0) for the later
+        // steps of the dW-only form, covers it.  For step 1 with the addend,
+        // step 0's addend loads come after the X of step 1 as well, and the
+        // wait is only stricter.  Steps past the slab end are still requested
+        // (they read zeros; their stores fall outside the range), which keeps
+        // every step's count identical.
+        if (kDX || j == 0)
+            wait_vmcnt<4>();
+        else
+            wait_vmcnt<0>();
         const uint32_t xa = ring_base + static_cast<uint32_t>((((j & 1) * 4) * kWave + lane) * 16);
         f32x4 xc[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) xc[rr] = lds_read_b128(xa + rr * kWave * 16);
         // The wait names every register the reads above return, so no use
         // of them can be scheduled before the data has arrived.
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
-                       "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]), "+v"(pa[1][1]),
-                       "+v"(pbv[0]), "+v"(pbv[1])::"memory");
+        if constexpr (kDX && kDW)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
+                           "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]), "+v"(pa[1][1]),
+                           "+v"(pbv[0]), "+v"(pbv[1])::"memory");
+        else if constexpr (kDX)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
+                           "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]),
+                           "+v"(pa[1][1])::"memory");
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(pbv[0]),
+                           "+v"(pbv[1])::"memory");
         lds_signal(consumed_addr + 4 * slot, lane);
-        uint2 av[4];
+        uint2 av[4] = {};
         const int d_range = range_elems(rows_left) * 2;
         if constexpr (kAddend) {
             const __amdgpu_buffer_rsrc_t ars = make_rsrc32(a_cur, d_range);
@@ -585,26 +617,30 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         for (int i = 0; i < 4; ++i) {
             // dX for column variant i: the RMS term c_t * x in FP32, then
             // the 96 exact partial products.
-            f32x4 acc = f32x4{ce[0] * xc[0][i], ce[1] * xc[1][i], ce[2] * xc[2][i],
-                              ce[3] * xc[3][i]};
+            f32x4 acc = {};
+            if constexpr (kDX) {
+                acc = f32x4{ce[0] * xc[0][i], ce[1] * xc[1][i], ce[2] * xc[2][i], ce[3] * xc[3][i]};
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int p = 0; p < 2; ++p) acc = mfma(pa[p][b], bw[i][b], acc);
+                    for (int p = 0; p < 2; ++p) acc = mfma(pa[p][b], bw[i][b], acc);
+            }
 
             // dW: x of column variant i split into BF16 hi/lo, packed
             // [hi r0..r3 | lo r0..r3], against each P part.
-            uint32_t hb[4];
-            float lo[4];
+            if constexpr (kDW) {
+                uint32_t hb[4];
+                float lo[4];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) tf32_split(xc[rr][i], hb[rr], lo[rr]);
-            const u32x4 ax = u32x4{hi_halves(hb[0], hb[1]), hi_halves(hb[2], hb[3]),
-                                   hi_halves(__float_as_uint(lo[0]), __float_as_uint(lo[1])),
-                                   hi_halves(__float_as_uint(lo[2]), __float_as_uint(lo[3]))};
+                for (int rr = 0; rr < 4; ++rr) tf32_split(xc[rr][i], hb[rr], lo[rr]);
+                const u32x4 ax = u32x4{hi_halves(hb[0], hb[1]), hi_halves(hb[2], hb[3]),
+                                       hi_halves(__float_as_uint(lo[0]), __float_as_uint(lo[1])),
+                                       hi_halves(__float_as_uint(lo[2]), __float_as_uint(lo[3]))};
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int p = 0; p < 2; ++p) accw[i][b] = mfma(ax, pb[p][b], accw[i][b]);
+                    for (int p = 0; p < 2; ++p) accw[i][b] = mfma(ax, pb[p][b], accw[i][b]);
+            }
 
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -621,11 +657,13 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         }
         // One rounding to BF16 per element (above), then 8-byte range-checked
         // stores: rows past the slab end are dropped.
-        const __amdgpu_buffer_rsrc_t drs = make_rsrc32(d_cur, d_range);
+        if constexpr (kDX) {
+            const __amdgpu_buffer_rsrc_t drs = make_rsrc32(d_cur, d_range);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[rr][0], packed[rr][1]}, drs, doff[rr],
-                                                  0, MHCPB_DX_AUX);
+            for (int rr = 0; rr < 4; ++rr)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[rr][0], packed[rr][1]}, drs,
+                                                      doff[rr], 0, MHCPB_DX_AUX);
+        }
         d_cur += kStepRows * row_bytes_d;
         ready_seen = lds_read_u32(ready_addr + 4 * ((j + 1) % kSlots));
     }
@@ -637,6 +675,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     // Partial dW of this slab, written once to workspace slab s.  Lane
     // (c16, g), element e of block jb is column kw + 16 g + 4 e + i of
     // j = 16 jb + c16.
+    if constexpr (!kDW) return;
     float *slab = ws + static_cast<int64_t>(s) * kProjCols * K;
     const int64_t cbase = kw + 16 * g;
 #pragma unroll
@@ -689,17 +728,32 @@ void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
 }
 
 template <int NW>
-hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t start,
-                               hipEvent_t stop) {
+hipError_t launch_projection_t(const Plan &p, const Args &a, Outputs out, hipStream_t stream,
+                               hipEvent_t start, hipEvent_t stop) {
     constexpr int cols = NW * 64;
     const dim3 grid(static_cast<unsigned>((p.K + cols - 1) / cols), static_cast<unsigned>(p.S));
     const dim3 block((NW + 1) * kWave);
-    if (a.addend)
-        launch(projection_kernel<NW, true>, grid, block, stream, start, stop, a.x, a.w, a.grad_proj,
-               a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L);
-    else
-        launch(projection_kernel<NW, false>, grid, block, stream, start, stop, a.x, a.w,
-               a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L);
+#define MHCPB_LAUNCH(ADD, DX, DW)                                                               \
+    launch(projection_kernel<NW, ADD, DX, DW>, grid, block, stream, start, stop, a.x, a.w,      \
+           a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L)
+    switch (out) {
+    case Outputs::kBoth:
+        if (a.addend)
+            MHCPB_LAUNCH(true, true, true);
+        else
+            MHCPB_LAUNCH(false, true, true);
+        break;
+    case Outputs::kDxOnly:
+        if (a.addend)
+            MHCPB_LAUNCH(true, true, false);
+        else
+            MHCPB_LAUNCH(false, true, false);
+        break;
+    case Outputs::kDwOnly:
+        MHCPB_LAUNCH(false, false, true);
+        break;
+    }
+#undef MHCPB_LAUNCH
     return hipGetLastError();
 }
 
@@ -710,9 +764,9 @@ hipError_t launch_projection_t(const Plan &p, const Args &a, hipStream_t stream,
 // Five compute waves and the producer make two workgroups per CU exactly
 // three waves per SIMD; at K = 20480 with 8 splits the grid is one full round
 // of two workgroups per CU on 256 CUs.
-hipError_t launch_projection(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t start,
-                             hipEvent_t stop) {
-    return launch_projection_t<5>(p, a, stream, start, stop);
+hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop) {
+    return launch_projection_t<5>(p, a, out, stream, start, stop);
 }
 
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop) {

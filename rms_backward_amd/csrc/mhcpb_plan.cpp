@@ -3,7 +3,9 @@
 // Follows the "Prepared class API" and "Requirements and tensor contract"
 // sections of the "DSv4.1 mHC projection/RMS backward" page: a plan is host
 // metadata; execute() checks the operands (alignment, disjointness), then
-// enqueues exactly two kernels and allocates nothing.
+// enqueues exactly two kernels and allocates nothing.  The split forms (dX
+// only, dW only) follow the split backward of the prime-kernels page ("FP8
+// weight cache, split backward, fused mHC stream gradient").
 #include <algorithm>
 #include <cstdint>
 #include <new>
@@ -26,46 +28,41 @@ bool aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) =
 
 bool overlap(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi; }
 
-mhcpb_status_t validate(const mhcpb::Plan &p, const float *x, const float *w,
-                        const float *grad_proj, const float *grad_r, const float *r,
-                        const uint16_t *dx, const float *dw, const uint16_t *addend,
-                        const void *ws, size_t ws_size) {
-    if (!x || !w || !grad_proj || !grad_r || !r || !dx || !dw || !ws)
-        return MHCPB_ERROR_INVALID_ARGUMENT;
-    if (ws_size < p.ws_bytes)
-        return MHCPB_ERROR_WORKSPACE;
-    const void *ptrs[] = {x, w, grad_proj, grad_r, r, dx, dw, ws, addend};
-    for (const void *q : ptrs)
-        if (q && !aligned(q))
+// One operand or output of a call: its address, its size in bytes, and
+// whether the call needs it (an optional one may be NULL).
+struct Operand {
+    const void *ptr;
+    uint64_t bytes;
+    bool required;
+};
+
+// Alignment, address wrap-around and pairwise overlap of the byte ranges of
+// the operands that are present, before any HIP call.
+mhcpb_status_t validate_ranges(const Operand *ops, int n) {
+    for (int i = 0; i < n; ++i)
+        if (ops[i].ptr && !aligned(ops[i].ptr))
             return MHCPB_ERROR_MISALIGNED;
-    const uint64_t T = static_cast<uint64_t>(p.T), K = static_cast<uint64_t>(p.K);
-    auto range = [](const void *q, uint64_t bytes) {
-        uintptr_t lo = reinterpret_cast<uintptr_t>(q);
-        return Range{lo, lo + static_cast<uintptr_t>(bytes)};
-    };
-    Range rs[9];
-    int n = 0;
-    rs[n++] = range(x, T * K * 4);
-    rs[n++] = range(w, 24 * K * 4);
-    rs[n++] = range(grad_proj, T * 32 * 4);
-    rs[n++] = range(grad_r, T * 4);
-    rs[n++] = range(r, T * 4);
-    rs[n++] = range(dx, T * K * 2);
-    rs[n++] = range(dw, 24 * K * 4);
-    rs[n++] = range(ws, p.ws_bytes);
-    if (addend)
-        rs[n++] = range(addend, T * K * 2);
+    Range rs[10];
+    int m = 0;
     for (int i = 0; i < n; ++i) {
-        if (rs[i].hi < rs[i].lo)  // address wrap-around
+        if (!ops[i].ptr)
+            continue;
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(ops[i].ptr);
+        const Range r{lo, lo + static_cast<uintptr_t>(ops[i].bytes)};
+        if (r.hi < r.lo)  // address wrap-around
             return MHCPB_ERROR_INVALID_ARGUMENT;
-        for (int j = i + 1; j < n; ++j)
+        rs[m++] = r;
+    }
+    for (int i = 0; i < m; ++i)
+        for (int j = i + 1; j < m; ++j)
             if (overlap(rs[i], rs[j]))
                 return MHCPB_ERROR_OVERLAP;
-    }
     return MHCPB_SUCCESS;
 }
 
-mhcpb_status_t run(mhcpb_plan_t plan, const float *x, const float *w,
+// Validates the operands the requested outputs need, then enqueues kernel 1
+// (and kernel 2 when dW is produced).
+mhcpb_status_t run(mhcpb_plan_t plan, mhcpb::Outputs out, const float *x, const float *w,
                    const float *grad_proj, const float *grad_r, const float *r,
                    uint16_t *dx, float *dw, const uint16_t *addend, void *ws,
                    size_t ws_size, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
@@ -73,13 +70,33 @@ mhcpb_status_t run(mhcpb_plan_t plan, const float *x, const float *w,
     if (!plan)
         return MHCPB_ERROR_INVALID_ARGUMENT;
     const mhcpb::Plan &p = plan->plan;
-    mhcpb_status_t st = validate(p, x, w, grad_proj, grad_r, r, dx, dw, addend, ws, ws_size);
+    const bool want_dx = out != mhcpb::Outputs::kDwOnly;
+    const bool want_dw = out != mhcpb::Outputs::kDxOnly;
+    const uint64_t T = static_cast<uint64_t>(p.T), K = static_cast<uint64_t>(p.K);
+    const Operand ops[] = {
+        {x, T * K * 4, true},
+        {grad_proj, T * 32 * 4, true},
+        {w, 24 * K * 4, want_dx},
+        {grad_r, T * 4, want_dx},
+        {r, T * 4, want_dx},
+        {dx, T * K * 2, want_dx},
+        {addend, T * K * 2, false},
+        {dw, 24 * K * 4, want_dw},
+        {ws, p.ws_bytes, want_dw},
+    };
+    constexpr int n = static_cast<int>(sizeof(ops) / sizeof(ops[0]));
+    for (int i = 0; i < n; ++i)
+        if (ops[i].required && !ops[i].ptr)
+            return MHCPB_ERROR_INVALID_ARGUMENT;
+    if (want_dw && ws_size < p.ws_bytes)
+        return MHCPB_ERROR_WORKSPACE;
+    const mhcpb_status_t st = validate_ranges(ops, n);
     if (st != MHCPB_SUCCESS)
         return st;
     mhcpb::Args a{x, w, grad_proj, grad_r, r, dx, dw, addend, static_cast<float *>(ws)};
-    if (mhcpb::launch_projection(p, a, stream, ev0, ev1) != hipSuccess)
+    if (mhcpb::launch_projection(p, a, out, stream, ev0, ev1) != hipSuccess)
         return MHCPB_ERROR_LAUNCH;
-    if (mhcpb::launch_reduce(p, a, stream, ev2) != hipSuccess)
+    if (want_dw && mhcpb::launch_reduce(p, a, stream, ev2) != hipSuccess)
         return MHCPB_ERROR_LAUNCH;
     return MHCPB_SUCCESS;
 }
@@ -135,8 +152,8 @@ mhcpb_status_t mhcpb_execute(mhcpb_plan_t plan, const float *x, const float *w,
                              const float *grad_proj, const float *grad_r, const float *r,
                              uint16_t *dx, float *dw, const uint16_t *grad_x_addend,
                              void *workspace, size_t workspace_size, hipStream_t stream) {
-    return run(plan, x, w, grad_proj, grad_r, r, dx, dw, grad_x_addend, workspace,
-               workspace_size, stream, nullptr, nullptr, nullptr);
+    return run(plan, mhcpb::Outputs::kBoth, x, w, grad_proj, grad_r, r, dx, dw, grad_x_addend,
+               workspace, workspace_size, stream, nullptr, nullptr, nullptr);
 }
 
 mhcpb_status_t mhcpb_execute_with_events(mhcpb_plan_t plan, const float *x, const float *w,
@@ -146,8 +163,23 @@ mhcpb_status_t mhcpb_execute_with_events(mhcpb_plan_t plan, const float *x, cons
                                          size_t workspace_size, hipStream_t stream,
                                          hipEvent_t before_k1, hipEvent_t after_k1,
                                          hipEvent_t after_k2) {
-    return run(plan, x, w, grad_proj, grad_r, r, dx, dw, grad_x_addend, workspace,
-               workspace_size, stream, before_k1, after_k1, after_k2);
+    return run(plan, mhcpb::Outputs::kBoth, x, w, grad_proj, grad_r, r, dx, dw, grad_x_addend,
+               workspace, workspace_size, stream, before_k1, after_k1, after_k2);
+}
+
+mhcpb_status_t mhcpb_execute_dx(mhcpb_plan_t plan, const float *x, const float *w,
+                                const float *grad_proj, const float *grad_r, const float *r,
+                                uint16_t *dx, const uint16_t *grad_x_addend,
+                                hipStream_t stream) {
+    return run(plan, mhcpb::Outputs::kDxOnly, x, w, grad_proj, grad_r, r, dx, nullptr,
+               grad_x_addend, nullptr, 0, stream, nullptr, nullptr, nullptr);
+}
+
+mhcpb_status_t mhcpb_execute_dw(mhcpb_plan_t plan, const float *x, const float *grad_proj,
+                                float *dw, void *workspace, size_t workspace_size,
+                                hipStream_t stream) {
+    return run(plan, mhcpb::Outputs::kDwOnly, x, nullptr, grad_proj, nullptr, nullptr, nullptr,
+               dw, nullptr, workspace, workspace_size, stream, nullptr, nullptr, nullptr);
 }
 
 const char *mhcpb_status_string(mhcpb_status_t status) {

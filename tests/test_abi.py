@@ -189,3 +189,41 @@ def test_null_plan_queries():
                                       ctypes.c_int32]
     assert lib.mhcpb_plan_create(None, 16, 4, 64) == m.MHCPB_ERROR_INVALID_ARGUMENT
     assert m.mhcpb_plan_destroy(None) is None
+
+
+def _exec_dx(plan, a):
+    return m.mhcpb_execute_dx(plan, a["x"], a["w"], a["grad_proj"], a["grad_r"], a["r"],
+                              a["dx"], a.get("addend"), 0, check=False)
+
+
+def _exec_dw(plan, a, ws_size):
+    return m.mhcpb_execute_dw(plan, a["x"], a["grad_proj"], a["dw"], a["ws"], ws_size, 0,
+                              check=False)
+
+
+@fake_addresses
+def test_split_forms_validate_their_own_operands():
+    """dX only needs x, w, grad_proj, grad_r, r, dx (and checks the addend when
+    given); dW only needs x, grad_proj, dw and the workspace.  Every error is
+    reported before a launch."""
+    plan = m.mhcpb_plan_create(64, 4, 64)
+    fb = _FakeBuffers(64, 64)
+    try:
+        for field in ("x", "w", "grad_proj", "grad_r", "r", "dx"):
+            assert _exec_dx(plan, fb.args(**{field: None})) == m.MHCPB_ERROR_INVALID_ARGUMENT
+            assert _exec_dx(plan, fb.args(**{field: fb.addr[field] + 4})) == m.MHCPB_ERROR_MISALIGNED
+        assert _exec_dx(plan, fb.args(addend=fb.addr["addend"] + 8)) == m.MHCPB_ERROR_MISALIGNED
+        assert _exec_dx(plan, fb.args(dx=fb.addr["x"] + 16)) == m.MHCPB_ERROR_OVERLAP
+        assert _exec_dx(plan, fb.args(addend=fb.addr["dx"])) == m.MHCPB_ERROR_OVERLAP
+        assert _exec_dx(None, fb.args()) == m.MHCPB_ERROR_INVALID_ARGUMENT
+        for field in ("x", "grad_proj", "dw", "ws"):
+            assert _exec_dw(plan, fb.args(**{field: None}), fb.ws_size) == \
+                m.MHCPB_ERROR_INVALID_ARGUMENT
+            assert _exec_dw(plan, fb.args(**{field: fb.addr[field] + 4}), fb.ws_size) == \
+                m.MHCPB_ERROR_MISALIGNED
+        assert _exec_dw(plan, fb.args(), fb.ws_needed - 1) == m.MHCPB_ERROR_WORKSPACE
+        assert _exec_dw(plan, fb.args(dw=fb.addr["ws"]), fb.ws_size) == m.MHCPB_ERROR_OVERLAP
+        assert _exec_dw(plan, fb.args(grad_proj=fb.addr["x"]), fb.ws_size) == m.MHCPB_ERROR_OVERLAP
+        assert _exec_dw(None, fb.args(), fb.ws_size) == m.MHCPB_ERROR_INVALID_ARGUMENT
+    finally:
+        m.mhcpb_plan_destroy(plan)
