@@ -5,7 +5,11 @@ leg of the benchmark use it; the GPU library never does.  It follows the
 formula of the "DSv4.1 mHC projection/RMS backward" cuDNN Frontend page
 (introduction):  P = grad_proj[:, :24], dX = P W + grad_r / (r K) X,
 dW = P^T X, with TF32 operands in ``mode="tf32"`` and exact FP32 operands in
-``mode="exact"``; results are FP64 with no final rounding.
+``mode="exact"``; results are FP64 with no final rounding.  ``forward`` is
+the map those are the gradient of: proj = X W^T (24 gate logits, TF32 operands
+in ``mode="tf32"``) and r = sqrt(mean(X^2) + eps) per row, the logits and RMS
+the "mhc_projection" entry of the prime-kernels pull request 15 page computes
+in one read of the streams.
 """
 from __future__ import annotations
 
@@ -56,6 +60,9 @@ def _load():
         lib.oracle_dx.restype = ctypes.c_int
         lib.oracle_dw.argtypes = [ctypes.c_int, i64, i64, f32p, f32p, f64p]
         lib.oracle_dw.restype = ctypes.c_int
+        lib.oracle_forward.argtypes = [ctypes.c_int, i64, i64, f32p, f32p,
+                                       ctypes.c_double, f64p, f64p]
+        lib.oracle_forward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -138,3 +145,23 @@ def backward(x, w, grad_proj, grad_r, r, addend=None, mode: str = "tf32"):
     K = np.shape(x)[1]
     return (dx(x, w, grad_proj, grad_r, r, K, addend=addend, mode=mode),
             dw(x, grad_proj, mode=mode))
+
+
+def forward(x, w, eps: float = 1e-6, mode: str = "tf32"):
+    """(proj [rows, 24], r [rows]) in FP64 for x [rows, K] and w [24, K].
+
+    ``eps`` is taken as given (pass the FP32 value a GPU call uses, widened).
+    """
+    lib = _load()
+    x, xp = _f32(x)
+    rows, K = x.shape
+    w, wp = _f32(w)
+    assert w.shape == (24, K)
+    proj = np.empty((rows, 24), dtype=np.float64)
+    r = np.empty((rows,), dtype=np.float64)
+    rc = lib.oracle_forward(_MODES[mode], rows, K, xp, wp, float(eps),
+                            proj.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                            r.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError("oracle_forward rejected its arguments")
+    return proj, r

@@ -24,6 +24,10 @@
  * grad_x_addend (prime-kernels pull request 15, "FP8 weight cache, split
  * backward, fused mHC stream gradient" section) is added to dX exactly.
  *
+ * oracle_forward is the map whose gradient these are: the 24 gate logits
+ * X W^T (TF32 operands in mode 1) and the row RMS sqrt(mean(x^2) + eps) in
+ * FP32-range arithmetic on the raw x (see its own comment).
+ *
  * Rounding here is done arithmetically (frexp / ldexp / nearbyint under
  * round-to-nearest-even), deliberately not by bit manipulation.
  *
@@ -34,6 +38,7 @@
  * order) are "parity unpinned": they are covered only by tolerances.
  */
 #include <fenv.h>
+#include <float.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -177,4 +182,58 @@ int oracle_mhcpb_backward(int mode, int64_t T, int64_t K,
     if (rc != 0)
         return rc;
     return oracle_dw(mode, T, K, x, grad_proj, dw);
+}
+
+/*
+ * The forward map of the stage: the 24 gate logits and the RMS of each row,
+ * in one pass over X.
+ *
+ * The backward page ("DSv4.1 mHC projection/RMS backward", introduction and
+ * "Requirements and tensor contract") takes r as the RMS "from forward" and
+ * defines dX = P W + grad_r / (r K) X and dW = P^T X: exactly the gradient of
+ *
+ *   proj[t, j] = sum_k X[t, k] W[j, k]            (j < 24)
+ *   r[t]       = sqrt(sum_k X[t, k]^2 / K + eps)
+ *
+ * with respect to X and W, since d r / d X[t, k] = X[t, k] / (r K).  The
+ * prime-kernels pull request 15 page (its list of kernels, "mhc_projection")
+ * computes the RMS and the gate logits of the streams in one read.  Where
+ * the normalisation by r is applied to the logits is not printed; the
+ * backward's separate grad_proj and grad_r mean the logits leave this map
+ * unnormalised, and that is the reading taken here.  As in the backward the
+ * product takes TF32 operands (mode 1) or the exact FP32 inputs (mode 0);
+ * the RMS always uses the raw FP32 x.  Everything is evaluated in FP64 with
+ * no final rounding, except one fact of the FP32 arithmetic the RMS is
+ * defined in: a sum of squares beyond the FP32 range makes r infinite.
+ *
+ *   x    [rows, K]  FP32
+ *   w    [24, K]    FP32
+ *   eps  the RMS epsilon (finite, >= 0)
+ *   proj [rows, 24] FP64 out
+ *   r    [rows]     FP64 out
+ */
+int oracle_forward(int mode, int64_t rows, int64_t K, const float *x,
+                   const float *w, double eps, double *proj, double *r)
+{
+    if (mode != 0 && mode != 1)
+        return -1;
+    if (rows < 0 || K <= 0 || !(eps >= 0.0) || isinf(eps))
+        return -1;
+    fesetround(FE_TONEAREST);
+    for (int64_t t = 0; t < rows; ++t) {
+        const float *xt = x + t * K;
+        for (int j = 0; j < ORACLE_PROJ_COLS; ++j) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += operand(xt[k], mode) * operand(w[(int64_t)j * K + k], mode);
+            proj[t * ORACLE_PROJ_COLS + j] = s;
+        }
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            ss += (double)xt[k] * (double)xt[k];
+        if (ss > (double)FLT_MAX)
+            ss = INFINITY;
+        r[t] = sqrt(ss / (double)K + eps);
+    }
+    return 0;
 }
