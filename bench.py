@@ -28,7 +28,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0
 METRIC = "µs/call and achieved HBM GB/s (% of peak) at T=4096, K=4×5120"
-KERNEL_SOURCE = os.path.join(ROOT, "rms_backward_amd", "csrc", "mhcpb_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "rms_backward_amd", "csrc", n)
+                  for n in ("mhcpb_kernels.hip", "mhcpb_device.h")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "projection_train_counters.json")
 
 
@@ -43,10 +44,13 @@ def algorithmic_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel source with comments, blank lines and trailing
-    spaces removed: it changes with the code, not with its comments."""
-    with open(KERNEL_SOURCE, encoding="utf-8") as f:
-        text = f.read()
+    """Hash of the backward kernels' source (the kernel file and the device
+    helpers it includes) with comments, blank lines and trailing spaces
+    removed: it changes with the code, not with its comments."""
+    text = ""
+    for path in KERNEL_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
     code = "\n".join(ln for ln in lines if ln)
