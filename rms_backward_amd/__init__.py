@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libmhcpb.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m rms_backward_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python rms_backward_amd/build.py` "
         "(hipcc, gfx950) before using rms_backward_amd")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -40,6 +40,8 @@ EXPORTED = (
     "mhcpb_plan_create", "mhcpb_plan_destroy", "mhcpb_workspace_bytes",
     "mhcpb_plan_split_count", "mhcpb_execute", "mhcpb_execute_with_events",
     "mhcpb_execute_dx", "mhcpb_execute_dw", "mhcpb_status_string",
+    "mhcpb_forward_workspace_bytes", "mhcpb_forward", "mhcpb_forward_with_events",
+    "mhcpb_forward_prepare_weight", "mhcpb_forward_prepared",
 )
 
 _vp = ctypes.c_void_p
@@ -61,6 +63,18 @@ _lib.mhcpb_execute_dx.argtypes = [_vp] * 8 + [_vp]
 _lib.mhcpb_execute_dx.restype = ctypes.c_int
 _lib.mhcpb_execute_dw.argtypes = [_vp] * 5 + [ctypes.c_size_t, _vp]
 _lib.mhcpb_execute_dw.restype = ctypes.c_int
+_lib.mhcpb_forward_workspace_bytes.argtypes = [_vp, ctypes.POINTER(ctypes.c_size_t)]
+_lib.mhcpb_forward_workspace_bytes.restype = ctypes.c_int
+_FWD_ARGS = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.mhcpb_forward.argtypes = _FWD_ARGS
+_lib.mhcpb_forward.restype = ctypes.c_int
+_lib.mhcpb_forward_with_events.argtypes = _FWD_ARGS + [_vp, _vp, _vp]
+_lib.mhcpb_forward_with_events.restype = ctypes.c_int
+_lib.mhcpb_forward_prepare_weight.argtypes = [_vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.mhcpb_forward_prepare_weight.restype = ctypes.c_int
+_lib.mhcpb_forward_prepared.argtypes = [_vp, _vp, _vp, ctypes.c_size_t, ctypes.c_float, _vp,
+                                        _vp, _vp]
+_lib.mhcpb_forward_prepared.restype = ctypes.c_int
 _lib.mhcpb_status_string.argtypes = [ctypes.c_int]
 _lib.mhcpb_status_string.restype = ctypes.c_char_p
 
@@ -165,4 +179,53 @@ def mhcpb_execute_dw(plan, x, grad_proj, dw, workspace, workspace_size: int, str
                                int(workspace_size), stream)
     if check and st != MHCPB_SUCCESS:
         raise MhcpbError(st, "mhcpb_execute_dw")
+    return st
+
+
+def mhcpb_forward_workspace_bytes(plan: int) -> int:
+    n = ctypes.c_size_t()
+    st = _lib.mhcpb_forward_workspace_bytes(plan, ctypes.byref(n))
+    if st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_forward_workspace_bytes")
+    return n.value
+
+
+def mhcpb_forward(plan, x, w, eps: float, proj, r, workspace, workspace_size: int,
+                  stream: int = 0, check: bool = True) -> int:
+    """Enqueue the forward map (weight split, then the pass over X)."""
+    st = _lib.mhcpb_forward(plan, _ptr(x), _ptr(w), float(eps), _ptr(proj), _ptr(r),
+                            _ptr(workspace), int(workspace_size), stream)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_forward")
+    return st
+
+
+def mhcpb_forward_with_events(plan, x, w, eps: float, proj, r, workspace, workspace_size: int,
+                              stream: int, before_split: int | None, before_pass: int | None,
+                              after_pass: int | None, check: bool = True) -> int:
+    """mhcpb_forward with caller-owned hipEvent_t handles on the dispatches."""
+    st = _lib.mhcpb_forward_with_events(plan, _ptr(x), _ptr(w), float(eps), _ptr(proj),
+                                        _ptr(r), _ptr(workspace), int(workspace_size), stream,
+                                        before_split, before_pass, after_pass)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_forward_with_events")
+    return st
+
+
+def mhcpb_forward_prepare_weight(plan, w, wsplit, wsplit_size: int, stream: int = 0,
+                                 check: bool = True) -> int:
+    """Write the TF32 split of W (two BF16 planes) into wsplit."""
+    st = _lib.mhcpb_forward_prepare_weight(plan, _ptr(w), _ptr(wsplit), int(wsplit_size), stream)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_forward_prepare_weight")
+    return st
+
+
+def mhcpb_forward_prepared(plan, x, wsplit, wsplit_size: int, eps: float, proj, r,
+                           stream: int = 0, check: bool = True) -> int:
+    """The pass over X with a weight split prepared earlier."""
+    st = _lib.mhcpb_forward_prepared(plan, _ptr(x), _ptr(wsplit), int(wsplit_size), float(eps),
+                                     _ptr(proj), _ptr(r), stream)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_forward_prepared")
     return st

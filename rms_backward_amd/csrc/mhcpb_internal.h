@@ -55,6 +55,21 @@ hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStrea
 // takes the end time of the dispatch.
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop);
 
+// Columns of a row of the forward's weight planes: K rounded up to whole
+// 64-column chunks (the padding is zero).
+inline int64_t forward_padded_cols(int64_t K) { return (K + 63) / 64 * 64; }
+
+// Forward, kernel 0: W [24, K] FP32 -> its TF32 split as two BF16 planes
+// (high parts, then low parts, 24 rows of forward_padded_cols(K) each) in
+// wsplit.
+hipError_t launch_split_weight(const Plan &p, const float *w, uint16_t *wsplit, hipStream_t stream,
+                               hipEvent_t start, hipEvent_t stop);
+// Forward, kernel 1: proj [T, 32] (logits in columns 0..23, zeros in 24..31)
+// and r [T] from X and the split W, in one pass over X.
+hipError_t launch_forward(const Plan &p, const float *x, const uint16_t *wsplit, float *proj,
+                          float *r, float eps, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop);
+
 }  // namespace mhcpb
 
 struct mhcpb_plan_s {

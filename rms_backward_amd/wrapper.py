@@ -10,8 +10,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (mhcpb_execute, mhcpb_plan_create, mhcpb_plan_destroy,
-               mhcpb_workspace_bytes)
+from . import (mhcpb_execute, mhcpb_forward, mhcpb_forward_prepare_weight,
+               mhcpb_forward_prepared, mhcpb_forward_workspace_bytes, mhcpb_plan_create,
+               mhcpb_plan_destroy, mhcpb_workspace_bytes)
 
 PROJ_COLS = 24
 
@@ -24,6 +25,7 @@ class Plan:
         self.K = self.streams * self.hidden
         self.handle = mhcpb_plan_create(self.T, self.streams, self.hidden)
         self.workspace_bytes = mhcpb_workspace_bytes(self.handle)
+        self.forward_workspace_bytes = mhcpb_forward_workspace_bytes(self.handle)
 
     def close(self):
         if self.handle:
@@ -38,6 +40,24 @@ class Plan:
 
     def alloc_workspace(self, device) -> torch.Tensor:
         return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device)
+
+    def alloc_forward_workspace(self, device) -> torch.Tensor:
+        return torch.empty(self.forward_workspace_bytes, dtype=torch.uint8, device=device)
+
+    def forward(self, x, w, eps, proj, r, workspace, stream=None):
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        return mhcpb_forward(self.handle, x, w, eps, proj, r, workspace, workspace.numel(),
+                             s.cuda_stream)
+
+    def prepare_weight(self, w, wsplit, stream=None):
+        s = stream if stream is not None else torch.cuda.current_stream(w.device)
+        return mhcpb_forward_prepare_weight(self.handle, w, wsplit, wsplit.numel(),
+                                            s.cuda_stream)
+
+    def forward_prepared(self, x, wsplit, eps, proj, r, stream=None):
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        return mhcpb_forward_prepared(self.handle, x, wsplit, wsplit.numel(), eps, proj, r,
+                                      s.cuda_stream)
 
     def execute(self, x, w, grad_proj, grad_r, r, dx, dw, workspace,
                 grad_x_addend=None, stream=None):
@@ -59,3 +79,19 @@ def mhc_projection_backward(x, w, grad_proj, grad_r, r, grad_x_addend=None, stre
     ws = plan.alloc_workspace(x.device)
     plan.execute(x, w, grad_proj, grad_r, r, dx, dw, ws, grad_x_addend, stream)
     return dx, dw
+
+
+def mhc_projection_forward(x, w, eps: float = 1e-6, stream=None):
+    """Allocate outputs and workspace, run the forward map, return (proj, r).
+
+    proj is FP32 [T, 32] (logits in columns 0..23, zeros in 24..31), r is
+    FP32 [T].
+    """
+    T, K = x.shape
+    assert K % 4 == 0
+    plan = Plan(T, 4, K // 4)
+    proj = torch.empty(T, 32, dtype=torch.float32, device=x.device)
+    r = torch.empty(T, dtype=torch.float32, device=x.device)
+    ws = plan.alloc_forward_workspace(x.device)
+    plan.forward(x, w, eps, proj, r, ws, stream)
+    return proj, r

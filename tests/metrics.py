@@ -52,3 +52,23 @@ def dw_accumulation_bound(abs_sum, rows_per_slab, splits):
     at most (rows_per_slab + splits + 64) roundings of 2^-24, each bounded by
     the sum of |products|.  Exact TF32 products are assumed."""
     return (rows_per_slab + splits + 64) * 2.0 ** -24 * np.asarray(abs_sum, dtype=np.float64)
+
+
+# ---- forward map (proj = X W^T with TF32 operands, r = RMS) ----------------
+# The GPU adds exact products in FP32 along chains of a few thousand
+# additions, whose rounding errors grow like 2^-24 sqrt(n) relative to the
+# partial sums: about 1e-6 of a logit at K = 20480.  The bounds below sit a
+# decade or more above that and a decade below what a dropped BF16 low part
+# (about 1e-3) or skipped TF32 rounding (about 3e-4) would give.
+FWD_PROJ_FROB = 1e-5
+FWD_PROJ_ROW = 1e-4
+FWD_PROJ_ELEM = 1e-4
+
+
+def fwd_r_rel_bound(K):
+    """Worst-case relative error of r: the FP32 sum of K positive squares in
+    chains of at most K/4 + 64 additions (relative error <= n 2^-24), halved
+    by the square root, plus one rounding each for the division by K, eps
+    and the square root."""
+    u = 2.0 ** -24
+    return (K / 4 + 64) * u / 2 + 3 * u

@@ -227,3 +227,79 @@ def test_split_forms_validate_their_own_operands():
         assert _exec_dw(None, fb.args(), fb.ws_size) == m.MHCPB_ERROR_INVALID_ARGUMENT
     finally:
         m.mhcpb_plan_destroy(plan)
+
+
+def test_forward_workspace_is_the_two_weight_planes():
+    for T, hidden in ((1, 2), (4096, 5120), (65536, 512)):
+        plan = m.mhcpb_plan_create(T, 4, hidden)
+        try:
+            kp = (4 * hidden + 63) // 64 * 64   # rows padded to whole 64-column chunks
+            assert m.mhcpb_forward_workspace_bytes(plan) == 2 * 24 * kp * 2
+        finally:
+            m.mhcpb_plan_destroy(plan)
+
+
+class _FakeForward:
+    """Disjoint, aligned fake device addresses for the forward's operands."""
+
+    def __init__(self, T, hidden):
+        K = 4 * hidden
+        plan = m.mhcpb_plan_create(T, 4, hidden)
+        self.ws_needed = m.mhcpb_forward_workspace_bytes(plan)
+        m.mhcpb_plan_destroy(plan)
+        sizes = dict(x=T * K * 4, w=24 * K * 4, proj=T * 128, r=T * 4, ws=self.ws_needed)
+        base = 1 << 41
+        self.addr, self.size = {}, sizes
+        for k, n in sizes.items():
+            self.addr[k] = base
+            base += (n + 4095) // 4096 * 4096 + 4096
+
+    def args(self, **over):
+        a = dict(self.addr)
+        a.update(over)
+        return a
+
+
+def _fwd(plan, a, ws_size, eps=1e-6):
+    return m.mhcpb_forward(plan, a["x"], a["w"], eps, a["proj"], a["r"], a["ws"], ws_size, 0,
+                           check=False)
+
+
+@fake_addresses
+def test_forward_validates_before_any_launch():
+    plan = m.mhcpb_plan_create(64, 4, 64)
+    fb = _FakeForward(64, 64)
+    ws = fb.ws_needed
+    try:
+        assert _fwd(None, fb.args(), ws) == m.MHCPB_ERROR_INVALID_ARGUMENT
+        for field in ("x", "w", "proj", "r", "ws"):
+            assert _fwd(plan, fb.args(**{field: None}), ws) == m.MHCPB_ERROR_INVALID_ARGUMENT
+            for off in (4, 8):
+                assert _fwd(plan, fb.args(**{field: fb.addr[field] + off}), ws) == \
+                    m.MHCPB_ERROR_MISALIGNED
+        for eps in (-1e-6, float("nan"), float("inf"), -float("inf")):
+            assert _fwd(plan, fb.args(), ws, eps=eps) == m.MHCPB_ERROR_INVALID_ARGUMENT
+        assert _fwd(plan, fb.args(), ws - 1) == m.MHCPB_ERROR_WORKSPACE
+        for a, b in (("x", "proj"), ("proj", "r"), ("ws", "w"), ("x", "ws"), ("r", "x")):
+            over = {b: fb.addr[a] + fb.size[a] - 16}
+            assert _fwd(plan, fb.args(**over), ws) == m.MHCPB_ERROR_OVERLAP, (a, b)
+        # the two halves check only their own operands
+        st = m.mhcpb_forward_prepare_weight(plan, fb.addr["w"], fb.addr["ws"] + 4, ws, 0,
+                                            check=False)
+        assert st == m.MHCPB_ERROR_MISALIGNED
+        st = m.mhcpb_forward_prepare_weight(plan, fb.addr["w"], fb.addr["w"] + 16, ws, 0,
+                                            check=False)
+        assert st == m.MHCPB_ERROR_OVERLAP
+        st = m.mhcpb_forward_prepare_weight(plan, None, fb.addr["ws"], ws, 0, check=False)
+        assert st == m.MHCPB_ERROR_INVALID_ARGUMENT
+        st = m.mhcpb_forward_prepared(plan, fb.addr["x"], fb.addr["ws"], ws, float("nan"),
+                                      fb.addr["proj"], fb.addr["r"], 0, check=False)
+        assert st == m.MHCPB_ERROR_INVALID_ARGUMENT
+        st = m.mhcpb_forward_prepared(plan, fb.addr["x"], fb.addr["ws"], ws - 2, 1e-6,
+                                      fb.addr["proj"], fb.addr["r"], 0, check=False)
+        assert st == m.MHCPB_ERROR_WORKSPACE
+        st = m.mhcpb_forward_prepared(plan, fb.addr["x"], fb.addr["ws"], ws, 1e-6,
+                                      fb.addr["x"] + 64, fb.addr["r"], 0, check=False)
+        assert st == m.MHCPB_ERROR_OVERLAP
+    finally:
+        m.mhcpb_plan_destroy(plan)

@@ -117,3 +117,52 @@ def forward_rms(x: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
 def bf16_bits(t: torch.Tensor) -> torch.Tensor:
     """Reinterpret a BF16 tensor as its uint16 bit patterns (int16 storage)."""
     return t.view(torch.int16)
+
+
+# ---- inputs of the forward map (X and W as above, plus structured cases) ----
+
+def forward_inputs(w: Workload, device="cpu") -> dict:
+    """X [T, K] and W [24, K] of workload ``w`` (the same draws as make())."""
+    full = make(w, device)
+    return dict(x=full["x"], w=full["w"])
+
+
+def odd_integers(shape, seed: int, limit: int = 2047) -> torch.Tensor:
+    """Odd integers in [-limit, limit] as FP32 (11 significant bits at most,
+    so a TF32 value has both a BF16 high and a nonzero low part)."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    v = torch.randint(0, (limit + 1) // 2, shape, generator=g) * 2 + 1
+    sign = torch.randint(0, 2, shape, generator=g) * 2 - 1
+    return (v * sign).to(torch.float32)
+
+
+def sparse_signs(shape, seed: int, nonzero: float = 0.25) -> torch.Tensor:
+    """Entries in {-1, 0, +1} with the given fraction of nonzeros, FP32."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    keep = torch.rand(shape, generator=g) < nonzero
+    sign = torch.randint(0, 2, shape, generator=g) * 2 - 1
+    return (keep * sign).to(torch.float32)
+
+
+def low_bit_values(shape, seed: int) -> torch.Tensor:
+    """N(0, 1) FP32 values whose low 13 fraction bits are random, with a
+    quarter of them set to exact TF32 ties (bit 12 set, bits 0..11 clear)."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    u = v.view(torch.int32)
+    tie = torch.rand(shape, generator=g) < 0.25
+    u[tie] = (u[tie] & ~0x1FFF) | 0x1000
+    return v
+
+
+def one_hot_rows(T: int, K: int, seed: int) -> torch.Tensor:
+    """[T, K] FP32 with one low-bit value per row at a random column."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    cols = torch.randint(0, K, (T,), generator=g)
+    x = torch.zeros(T, K, dtype=torch.float32)
+    x[torch.arange(T), cols] = low_bit_values((T,), seed + 1)
+    return x
