@@ -1,6 +1,7 @@
 """Benchmark of the DSv4.1 mHC projection/RMS backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
+                    [--stage backward|forward] [--form fused|split]
 
 One step is one call of mhcpb_execute (kernel 1 + kernel 2) on the synthetic
 workload, with every input already resident in HBM.  Prints ONE JSON line:
@@ -208,6 +209,158 @@ def run_split(args, wl, inp, plan, S, dx, dw, ws) -> dict:
     }
 
 
+FORWARD_METRIC = ("forward map: µs/call and achieved HBM GB/s (% of peak) at "
+                  "T=4096, K=4×5120")
+FORWARD_SOURCES = [os.path.join(ROOT, "rms_backward_amd", "csrc", n)
+                   for n in ("mhcpb_forward.hip", "mhcpb_device.h")]
+FORWARD_COUNTERS_FILE = os.path.join(ROOT, "profiles", "forward_train_counters.json")
+
+
+def forward_bytes(T: int, K: int) -> tuple[int, int]:
+    """(whole call, pass over X) algorithmic bytes of the forward map: the
+    weight split reads W and writes its two BF16 planes (rows padded to whole
+    64-column chunks); the pass reads X and the planes once and writes proj
+    [T, 32] and r."""
+    kp = (K + 63) // 64 * 64
+    planes = 2 * 24 * kp * 2
+    pass_bytes = T * K * 4 + planes + T * 32 * 4 + T * 4
+    return pass_bytes + 24 * K * 4 + planes, pass_bytes
+
+
+def forward_source_hash() -> str:
+    text = ""
+    for path in FORWARD_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            text += f.read() + "\n"
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()[:16]
+
+
+def forward_traffic(workload: str):
+    """HBM bytes per pass-kernel launch from the committed counter summary,
+    if taken on the current forward source; otherwise None."""
+    try:
+        with open(FORWARD_COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != forward_source_hash():
+        return None
+    if rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def forward_cpu_baseline(x, w, rows: int, T: int, K: int):
+    """Time the FP64 oracle's forward (as it is, one thread) on `rows` rows."""
+    import oracle
+    rows = min(rows, T)
+    xs = x[:rows].cpu().numpy()
+    ws = w.cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.forward(xs, ws, eps=1e-6, mode="tf32")
+    dt = time.perf_counter() - t0
+    call_bytes, _ = forward_bytes(T, K)
+    frac = rows / T
+    return {
+        "value": round(call_bytes * frac / dt / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {rows} of {T} rows, all {K} columns: proj and r, TF32-mode "
+                   f"FP64 oracle, one thread; {dt:.2f} s"),
+        "us_per_call_extrapolated": round(dt / frac * 1e6, 1),
+    }
+
+
+def run_forward(args, wl) -> dict:
+    """The forward map: per step one mhcpb_forward call (weight split, then
+    the pass over X)."""
+    import torch
+    import workloads
+    from rms_backward_amd import mhcpb_forward_with_events
+    from rms_backward_amd.wrapper import Plan
+
+    T, K = wl.T, wl.K
+    inp = workloads.forward_inputs(wl, "cuda")
+    x, w = inp["x"], inp["w"]
+    plan = Plan(T, wl.streams, wl.hidden)
+    proj = torch.full((T, 32), float("nan"), dtype=torch.float32, device="cuda")
+    r = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = plan.alloc_forward_workspace("cuda")
+    eps = 1e-6
+    call = lambda: plan.forward(x, w, eps, proj, r, ws)
+    for _ in range(args.warmup):
+        call()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us_per_call = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    hev = HipEvents()
+    n = args.steps
+    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b, c in evs:
+        mhcpb_forward_with_events(plan.handle, x, w, eps, proj, r, ws, ws.numel(),
+                                  stream.cuda_stream, a, b, c)
+    torch.cuda.synchronize()
+    split_ms = [hev.elapsed_ms(a, b) for a, b, _ in evs]
+    pass_ms = [hev.elapsed_ms(b, c) for _, b, c in evs]
+    for trio in evs:
+        for e in trio:
+            hev.destroy(e)
+    split_us = sum(split_ms) / n * 1e3
+    pass_us = sum(pass_ms) / n * 1e3
+    call_bytes, pass_bytes = forward_bytes(T, K)
+    gbps = call_bytes / (us_per_call * 1e-6) / 1e9
+    pass_gbps = pass_bytes / (pass_us * 1e-6) / 1e9
+    return {
+        "metric": FORWARD_METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_call / 1e3, 6),
+        "us_per_call": round(us_per_call, 2),
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "tf32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name} forward: T={T} tokens, {wl.streams} streams x hidden "
+                         f"{wl.hidden} (K={K}); X, W FP32 in, proj [T, 32] and r FP32 out"),
+            "stage": "forward", "T": T, "K": K,
+            "bytes_per_call": call_bytes,
+            "split_us_with_gap": round(split_us, 2), "pass_us": round(pass_us, 2),
+            "timed_wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(pass_gbps, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(pass_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": forward_traffic(wl.name),
+            "kernel": "forward pass over X (forward_kernel)",
+            "bytes_per_launch": pass_bytes,
+        },
+        "_inputs": (x, w),
+    }
+
+
 def run_copy_calibration(nbytes: int, reps: int):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -231,6 +384,9 @@ def main(argv=None):
     ap.add_argument("--form", choices=("fused", "split"), default="fused",
                     help="fused: mhcpb_execute per step; split: mhcpb_execute_dx then "
                          "mhcpb_execute_dw per step (X read twice)")
+    ap.add_argument("--stage", choices=("backward", "forward"), default="backward",
+                    help="backward: the stage (default); forward: the map it differentiates "
+                         "(mhcpb_forward: proj = X W^T and r per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter scaling)")
     args = ap.parse_args(argv)
@@ -254,7 +410,18 @@ def main(argv=None):
 
     wl = workloads.WORKLOADS[args.workload]
     T, K = wl.T, wl.K
-    print(f"bench: workload {wl.name} T={T} K={K}", file=sys.stderr, flush=True)
+    print(f"bench: workload {wl.name} T={T} K={K} stage {args.stage}", file=sys.stderr,
+          flush=True)
+    if args.stage == "forward":
+        out = run_forward(args, wl)
+        x, w = out.pop("_inputs")
+        if not args.no_cpu_baseline:
+            print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+            out["cpu_baseline"] = forward_cpu_baseline(x, w, args.cpu_rows, T, K)
+        else:
+            out["cpu_baseline"] = None
+        print(json.dumps(out), flush=True)
+        return 0
     inp = workloads.make(wl, "cuda")
     plan = Plan(T, wl.streams, wl.hidden)
     S = mhcpb_plan_split_count(plan.handle)

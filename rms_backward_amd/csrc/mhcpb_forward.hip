@@ -6,10 +6,11 @@
 // prime-kernels pull request 15 page lists the RMS and the gate logits of the
 // streams as one pass, "mhc_projection").
 //
-// Kernel "split_weight": W [24, K] FP32 -> two BF16 planes, the high part of
-// TF32(W) (its upper 16 bits) and the exact low part, so that the main kernel
-// spends no arithmetic on W.  Both planes take the caller's workspace; their
-// rows are padded with zeros to a whole number of 64-column chunks.
+// Kernel "split_weight": W [24, K] FP32 -> the high part of TF32(W) (its
+// upper 16 bits) and the exact low part as BF16, laid out in the order the
+// main kernel's lanes load them, so that it spends no arithmetic on W and
+// reads it in whole cache lines.  It takes the caller's workspace, zero past
+// K up to a whole number of 64-column chunks.
 //
 // Kernel "forward_kernel": one workgroup per 16 tokens.  Its NW waves split
 // the K columns into 64-column chunks (wave w takes chunks w, w + NW, ...),
@@ -32,8 +33,9 @@
 // being computed, at no register cost.  One DMA instruction moves 8 rows x 128
 // contiguous bytes; the 16-byte segments of a row are XOR-swizzled so that the
 // A-operand reads (16 tokens at one segment) hit 16 different bank groups.
-// The W planes (read by every workgroup, L2-resident, rows padded with zeros
-// to whole chunks) are loaded into registers one chunk ahead.  Rows past T
+// W (read by every workgroup, L2-resident) is stored by split_weight in the
+// order of the MFMA operands, so each W load of a wave is 1 KB of
+// consecutive bytes, and is loaded into registers one chunk ahead.  Rows past T
 // fall outside the X buffer range, the columns past K of a ragged last chunk
 // take offsets outside it, and both read as zeros.
 #include "mhcpb_device.h"
@@ -45,7 +47,6 @@ namespace {
 constexpr int kFwdRows = 16;    // tokens per workgroup
 constexpr int kFwdChunk = 64;   // columns per step
 constexpr int kFwdDma = 4;      // LDS DMA instructions per step (16 rows x 256 bytes)
-constexpr int kFwdStages = 3;   // LDS ring stages per wave
 constexpr int kFwdWLoads = 6;   // 16-byte W loads per lane per step
 
 // Cache policy of the X stream (read once): non-temporal.
@@ -86,9 +87,11 @@ __device__ __forceinline__ u32x4 load_b128_untracked(i32x4 rs, uint32_t off) {
 // Waits until at most N vector memory requests are outstanding; names the
 // six W registers of a step, so their values count as produced here.
 template <int N>
-__device__ __forceinline__ void wait_vmcnt_w(u32x4 (&wv)[6]) {
+__device__ __forceinline__ void wait_vmcnt_w(const u32x4 (&wv)[6]) {
     asm volatile("s_waitcnt vmcnt(%6)"
-                 : "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]), "+v"(wv[4]), "+v"(wv[5])
+                 : "+v"(const_cast<u32x4 &>(wv[0])), "+v"(const_cast<u32x4 &>(wv[1])),
+                   "+v"(const_cast<u32x4 &>(wv[2])), "+v"(const_cast<u32x4 &>(wv[3])),
+                   "+v"(const_cast<u32x4 &>(wv[4])), "+v"(const_cast<u32x4 &>(wv[5]))
                  : "n"(N)
                  : "memory");
 }
@@ -98,40 +101,53 @@ __device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 
-// W [24, K] -> wsplit[0][j][k] = high parts, wsplit[1][j][k] = low parts,
-// planes of 24 rows of Kp = 64 ceil(K / 64) columns (n = 24 Kp elements
-// each); columns K .. Kp - 1 are zero, so a partial last chunk needs no mask
-// on the W side.  Eight elements per thread (K and Kp are multiples of 8, so
-// the eight are all inside or all padding).  Non-finite W keeps its class in
-// the high part (NaN as the quiet NaN) with a zero low part.
+// W [24, K] -> its TF32 split in the order the MFMA B operands are loaded:
+// for chunk c (64 columns), operand e = 3G + kind (G: column group of 32,
+// kind 0 = high parts of gates 0..15, 1 = low parts of gates 0..15, 2 = high
+// parts of gates 16..23 in lanes n < 8 and low parts in lanes n >= 8) and
+// lane l = 16q + n, the 16 bytes wtile[c][e][l] hold the eight BF16 parts of
+// that gate at columns 64c + 32G + 8q .. +7.  One W load of a wave is then
+// 1 KB of consecutive bytes.  Columns past K are zero, so a partial last
+// chunk needs no mask on the W side.  One 16-byte fragment per thread (K is
+// a multiple of 8, so its eight columns are all inside or all padding).
+// Non-finite W keeps its class in the high part (NaN as the quiet NaN) with
+// a zero low part.
 __global__ __launch_bounds__(256) void split_weight(const float *__restrict__ w,
-                                                    uint16_t *__restrict__ wsplit, int64_t K,
-                                                    int64_t Kp, int64_t n8) {
+                                                    u32x4 *__restrict__ wtile, int64_t K,
+                                                    int64_t nfrag) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= n8) return;
-    const int64_t j = (8 * i) / Kp, k = (8 * i) % Kp;
-    u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
-    if (k < K) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(w + j * K + k);
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(w + j * K + k + 4);
+    if (i >= nfrag) return;
+    const int lane = static_cast<int>(i % kWave);
+    const int e = static_cast<int>((i / kWave) % kFwdWLoads);
+    const int64_t c = i / (kWave * kFwdWLoads);
+    const int q = lane / 16, n = lane % 16;
+    const int G = e / 3, kind = e % 3;
+    const int gate = kind < 2 ? n : 16 + (n & 7);
+    const bool low = kind == 1 || (kind == 2 && n >= 8);
+    const int64_t col = kFwdChunk * c + 32 * G + 8 * q;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (col < K) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(w + gate * K + col);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(w + gate * K + col + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         uint32_t pk[8];  // hi | lo << 16
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk[e] = tf32_split_packed(v[e]);
-        hi = u32x4{lo_halves(pk[0], pk[1]), lo_halves(pk[2], pk[3]), lo_halves(pk[4], pk[5]),
-                   lo_halves(pk[6], pk[7])};
-        lo = u32x4{hi_halves(pk[0], pk[1]), hi_halves(pk[2], pk[3]), hi_halves(pk[4], pk[5]),
-                   hi_halves(pk[6], pk[7])};
+        for (int k = 0; k < 8; ++k) pk[k] = tf32_split_packed(v[k]);
+        out = low ? u32x4{hi_halves(pk[0], pk[1]), hi_halves(pk[2], pk[3]),
+                          hi_halves(pk[4], pk[5]), hi_halves(pk[6], pk[7])}
+                  : u32x4{lo_halves(pk[0], pk[1]), lo_halves(pk[2], pk[3]),
+                          lo_halves(pk[4], pk[5]), lo_halves(pk[6], pk[7])};
     }
-    reinterpret_cast<u32x4 *>(wsplit)[i] = hi;
-    reinterpret_cast<u32x4 *>(wsplit + 8 * n8)[i] = lo;
+    wtile[i] = out;
 }
 
-template <int NW>
+template <int NW, int NS>
 __global__ __launch_bounds__(NW * kWave) void forward_kernel(
     const float *__restrict__ x, const uint16_t *__restrict__ wsplit, float *__restrict__ proj,
     float *__restrict__ rout, int64_t T, int64_t K, float eps) {
-    __shared__ f32x4 xring[NW][kFwdStages][kFwdDma][kWave];
+    static_assert(NS >= 3, "X is requested at least two chunks ahead");
+    constexpr int DX = NS - 1;  // chunks of X requested ahead of the one computed
+    __shared__ f32x4 xring[NW][NS][kFwdDma][kWave];
     static_assert(sizeof(xring) >= NW * kWave * (2 * 16 + 4), "reduction area fits the ring");
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -171,21 +187,11 @@ __global__ __launch_bounds__(NW * kWave) void forward_kernel(
                 rd[G][h] = static_cast<uint32_t>((64 * (2 * a + G) + 8 * mi + (si ^ mi ^ a)) * 16);
             }
     }
-    // W: B lane (q, gate n16) loads 8 BF16 columns 32G + 8q .. of group G from
-    // the high plane and the low plane for gates 0..15, and for gates 16..23
-    // the high part (lanes n16 < 8) or the low part (lanes n16 >= 8) of gate
-    // 16 + n16 % 8.  The planes have rows of kp columns, zero past K.
-    // Offsets in bytes from the chunk's first column.
-    const int kp = kFwdChunk * nchunks;
+    // W: B operand e of chunk c for this lane is the 16 bytes at
+    // ((6c + e) 64 + lane) 16 of the tiled split (see split_weight).
     uint32_t woff[kFwdWLoads];
 #pragma unroll
-    for (int G = 0; G < 2; ++G) {
-        const int col = 32 * G + 8 * q;
-        woff[3 * G + 0] = static_cast<uint32_t>((n16 * kp + col) * 2);
-        woff[3 * G + 1] = static_cast<uint32_t>(((kProjCols + n16) * kp + col) * 2);
-        woff[3 * G + 2] =
-            static_cast<uint32_t>(((n16 < 8 ? 16 + n16 : kProjCols + 8 + n16) * kp + col) * 2);
-    }
+    for (int e = 0; e < kFwdWLoads; ++e) woff[e] = static_cast<uint32_t>((e * kWave + lane) * 16);
 
     const uint32_t ring = lds_addr(&xring[wave][0][0][0]);
     constexpr uint32_t kStageBytes = kFwdDma * kWave * 16;
@@ -204,9 +210,8 @@ __global__ __launch_bounds__(NW * kWave) void forward_kernel(
                 tail ? xoff_tail[rr] : xoff[rr], 0, 0, MHCPB_FWD_X_AUX);
     };
     auto load_w = [&](int c, u32x4 (&wv)[kFwdWLoads]) {
-        const int c0 = kFwdChunk * c;
-        const int n = c < nchunks ? 2 * kProjCols * kp - c0 : 0;
-        const i32x4 rs = rsrc_words(wsplit + c0, n * 2);
+        const int n = c < nchunks ? kFwdWLoads * kWave * 16 : 0;
+        const i32x4 rs = rsrc_words(wsplit + static_cast<int64_t>(c) * (kFwdWLoads * kWave * 8), n);
 #pragma unroll
         for (int e = 0; e < kFwdWLoads; ++e) wv[e] = load_b128_untracked(rs, woff[e]);
     };
@@ -215,17 +220,22 @@ __global__ __launch_bounds__(NW * kWave) void forward_kernel(
     f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};  // gates 16..23: high part | low part
     float ss = 0.f;                     // sum of x^2 of token n16, this lane's columns
 
-    // One step: chunk wave + NW j from ring stage j % 3 with the W of wcur;
-    // requests the W of the next chunk into wnext and the X two chunks on.
-    // Order of the vector memory requests: W(0), X(0), X(1) before the loop,
-    // then W(j + 1), X(j + 2) in step j.  X(j + 1) precedes W(j + 1), so the
-    // wait at the end of step j, vmcnt(4), leaves exactly X(j + 2) in flight:
-    // the next step finds its X in LDS and its W in registers.  Steps past
-    // the last chunk still request (an empty range: zeros), which keeps the
-    // count the same for every step.
-    auto step = [&](int j, const u32x4 (&wcur)[kFwdWLoads], u32x4 (&wnext)[kFwdWLoads]) {
+    // One step: chunk wave + NW j from ring stage j % NS with the W of wcur.
+    // Order of the vector memory requests: W(0), W(1), X(0) .. X(DX - 1)
+    // before the loop, then W(j + 2) (into wload), X(j + DX) in step j.  The
+    // wait at the end of step j must leave X(j + 1) in LDS and W(j + 1) (in
+    // wnext) in registers.  With DX = 2, X(j + 1) is the last request of step
+    // j - 1, so the 10 requests of step j stay in flight; with DX >= 3 W(j + 1)
+    // is the first request of step j - 1, so its 4 X requests and the 10 of
+    // step j stay in flight.  Steps past the last chunk still request (an
+    // empty range: zeros), which keeps every step's count the same.
+    constexpr int kStepWait = DX == 2 ? kFwdWLoads + kFwdDma : kFwdWLoads + 2 * kFwdDma;
+    // The last one or two steps of a wave (after the drain below) request
+    // nothing: their X and W were requested by the steps before them.
+    auto step = [&](int j, const u32x4 (&wcur)[kFwdWLoads], u32x4 (&wload)[kFwdWLoads],
+                    u32x4 (&wnext)[kFwdWLoads], bool prefetch) {
         const int c = wave + NW * j;
-        const uint32_t sb = ring + static_cast<uint32_t>(j % kFwdStages) * kStageBytes;
+        const uint32_t sb = ring + static_cast<uint32_t>(j % NS) * kStageBytes;
         f32x4 xv[2][2];
 #pragma unroll
         for (int G = 0; G < 2; ++G)
@@ -233,10 +243,12 @@ __global__ __launch_bounds__(NW * kWave) void forward_kernel(
             for (int h = 0; h < 2; ++h) xv[G][h] = lds_read_b128(sb + rd[G][h]);
         asm volatile("s_waitcnt lgkmcnt(0)"
                      : "+v"(xv[0][0]), "+v"(xv[0][1]), "+v"(xv[1][0]), "+v"(xv[1][1])::"memory");
-        compiler_fence();
-        load_w(c + NW, wnext);
-        issue_x(c + 2 * NW, (j + 2) % kFwdStages);
-        compiler_fence();
+        if (prefetch) {
+            compiler_fence();
+            load_w(c + 2 * NW, wload);
+            issue_x(c + DX * NW, (j + DX) % NS);
+            compiler_fence();
+        }
 #pragma unroll
         for (int G = 0; G < 2; ++G) {
             const float v[8] = {xv[G][0].x, xv[G][0].y, xv[G][0].z, xv[G][0].w,
@@ -260,23 +272,36 @@ __global__ __launch_bounds__(NW * kWave) void forward_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
         }
-        wait_vmcnt_w<kFwdDma>(wnext);
+        if (prefetch) wait_vmcnt_w<kStepWait>(wnext);
     };
 
-    u32x4 wa[kFwdWLoads], wb[kFwdWLoads];
+    // Three W register sets in rotation: step j computes with W(j), while
+    // W(j + 1) may still be arriving and W(j + 2) is requested.
+    u32x4 wa[kFwdWLoads], wb[kFwdWLoads], wc[kFwdWLoads];
     load_w(wave, wa);
+    load_w(wave + NW, wb);
     compiler_fence();
-    issue_x(wave, 0);
-    issue_x(wave + NW, 1);
-    wait_vmcnt_w<kFwdDma>(wa);
+#pragma unroll
+    for (int k = 0; k < DX; ++k) issue_x(wave + k * NW, k);
+    wait_vmcnt_w<kFwdDma * (DX - 1)>(wa);
     int j = 0;
-    for (; j + 1 < nsteps; j += 2) {
-        step(j, wa, wb);
-        step(j + 1, wb, wa);
+    for (; j + 2 < nsteps; j += 3) {
+        step(j, wa, wc, wb, true);
+        step(j + 1, wb, wa, wc, true);
+        step(j + 2, wc, wb, wa, true);
     }
-    if (j < nsteps) step(j, wa, wb);
-    // Every DMA of this wave has landed before the ring is reused below.
-    wait_vmcnt<0>();
+    // Every request of this wave lands here, before the last steps and
+    // before the ring is reused below.  The wait names every W register set:
+    // none may be reused before its last load has landed, and after it no
+    // load is in flight, so the branches below cannot meet one.
+    asm volatile("s_waitcnt vmcnt(0)"
+                 : "+v"(wa[0]), "+v"(wa[1]), "+v"(wa[2]), "+v"(wa[3]), "+v"(wa[4]), "+v"(wa[5]),
+                   "+v"(wb[0]), "+v"(wb[1]), "+v"(wb[2]), "+v"(wb[3]), "+v"(wb[4]), "+v"(wb[5]),
+                   "+v"(wc[0]), "+v"(wc[1]), "+v"(wc[2]), "+v"(wc[3]), "+v"(wc[4]), "+v"(wc[5])
+                 :
+                 : "memory");
+    if (j < nsteps) step(j, wa, wc, wb, false);
+    if (j + 1 < nsteps) step(j + 1, wb, wa, wc, false);
     __syncthreads();
 
     // Partial sums of each wave, then their sum in wave order by wave 0.
@@ -326,10 +351,10 @@ __global__ __launch_bounds__(NW * kWave) void forward_kernel(
 
 hipError_t launch_split_weight(const Plan &p, const float *w, uint16_t *wsplit, hipStream_t stream,
                                hipEvent_t start, hipEvent_t stop) {
-    const int64_t kp = forward_padded_cols(p.K);
-    const int64_t n8 = kProjCols * kp / 8;
-    const unsigned blocks = static_cast<unsigned>((n8 + 255) / 256);
-    launch(split_weight, dim3(blocks), dim3(256), stream, start, stop, w, wsplit, p.K, kp, n8);
+    const int64_t nfrag = forward_padded_cols(p.K) / kFwdChunk * kFwdWLoads * kWave;
+    const unsigned blocks = static_cast<unsigned>((nfrag + 255) / 256);
+    launch(split_weight, dim3(blocks), dim3(256), stream, start, stop, w,
+           reinterpret_cast<u32x4 *>(wsplit), p.K, nfrag);
     return hipGetLastError();
 }
 
@@ -339,8 +364,9 @@ hipError_t launch_forward(const Plan &p, const float *x, const uint16_t *wsplit,
                           float *r, float eps, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
     constexpr int NW = 8;
+    constexpr int NS = 3;
     const dim3 grid(static_cast<unsigned>((p.T + kFwdRows - 1) / kFwdRows));
-    launch(forward_kernel<NW>, grid, dim3(NW * kWave), stream, start, stop, x, wsplit, proj, r,
+    launch(forward_kernel<NW, NS>, grid, dim3(NW * kWave), stream, start, stop, x, wsplit, proj, r,
            p.T, p.K, eps);
     return hipGetLastError();
 }

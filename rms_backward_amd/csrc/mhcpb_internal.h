@@ -59,9 +59,9 @@ hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEv
 // 64-column chunks (the padding is zero).
 inline int64_t forward_padded_cols(int64_t K) { return (K + 63) / 64 * 64; }
 
-// Forward, kernel 0: W [24, K] FP32 -> its TF32 split as two BF16 planes
-// (high parts, then low parts, 24 rows of forward_padded_cols(K) each) in
-// wsplit.
+// Forward, kernel 0: W [24, K] FP32 -> its TF32 split (BF16 high and low
+// parts of 24 x forward_padded_cols(K) values, zero past K) in wsplit, in the
+// order the pass over X loads it.
 hipError_t launch_split_weight(const Plan &p, const float *w, uint16_t *wsplit, hipStream_t stream,
                                hipEvent_t start, hipEvent_t stop);
 // Forward, kernel 1: proj [T, 32] (logits in columns 0..23, zeros in 24..31)
