@@ -177,13 +177,15 @@ mhcpb_status_t mhcpb_execute_dw(mhcpb_plan_t plan, const float *x, const float *
  *   proj     [T, 32] FP32 out: logits in columns 0..23, +0 in 24..31 (the
  *            row layout of grad_proj), overwritten
  *   r        [T] FP32 out, overwritten
- *   workspace at least mhcpb_forward_workspace_bytes(plan) bytes (2 * 24 *
- *            Kp * 2 with Kp = K rounded up to a multiple of 64: the TF32
- *            split of W as BF16 high and low planes, rows zero-padded);
- *            contents undefined on entry, the split of w on exit
+ *   workspace at least mhcpb_forward_workspace_bytes(plan) bytes: ceil(K /
+ *            1024) x ceil(T / 16) x 2048, the partial logits and sums of
+ *            squares of each 1024-column tile (32 FP32 per token); contents
+ *            undefined on entry and on exit
  *
- * Two kernels on `stream`: the split of W, then the pass over X.  Each row's
- * results depend only on that row, W, eps and K (not on T or other rows).
+ * Two kernels on `stream`: one pass over X writing a partial per 1024-column
+ * tile and token, then their sum in tile order.  Each row's results depend
+ * only on that row, W, eps and K (not on T or other rows).  ceil(K / 1024) x
+ * ceil(T / 16) must stay below 2^31 (else MHCPB_ERROR_UNSUPPORTED).
  * Non-finite inputs give non-finite outputs where IEEE arithmetic on the TF32
  * operands does (a NaN in a row makes its 24 logits and r NaN); whether such
  * a logit is +-inf or NaN is not promised.  A sum of squares beyond the FP32
@@ -198,30 +200,14 @@ mhcpb_status_t mhcpb_forward(mhcpb_plan_t plan, const float *x, const float *w, 
 
 /*
  * mhcpb_forward with caller-owned events attached to the dispatches:
- * `before_split` takes the start time of the weight split, `before_pass` and
- * `after_pass` the start and end times of the pass over X.  Any may be NULL.
+ * `before_k1` and `after_k1` take the start and end times of the pass over X,
+ * `after_k2` the end time of the sum of the tiles.  Any may be NULL.
  */
 mhcpb_status_t mhcpb_forward_with_events(mhcpb_plan_t plan, const float *x, const float *w,
                                          float eps, float *proj, float *r, void *workspace,
                                          size_t workspace_size, hipStream_t stream,
-                                         hipEvent_t before_split, hipEvent_t before_pass,
-                                         hipEvent_t after_pass);
-
-/*
- * The two halves of mhcpb_forward, for callers that keep W fixed over many
- * calls (the weight-cache idea of the prime-kernels page, "FP8 weight cache,
- * split backward, fused mHC stream gradient": prepare once per weight update,
- * reuse across micro-batches).  mhcpb_forward_prepare_weight writes the split
- * of w into wsplit (mhcpb_forward_workspace_bytes(plan) bytes);
- * mhcpb_forward_prepared runs the pass over X with a wsplit so prepared for a
- * plan of the same K, and gives the bits mhcpb_forward gives.
- */
-mhcpb_status_t mhcpb_forward_prepare_weight(mhcpb_plan_t plan, const float *w, void *wsplit,
-                                            size_t wsplit_size, hipStream_t stream);
-
-mhcpb_status_t mhcpb_forward_prepared(mhcpb_plan_t plan, const float *x, const void *wsplit,
-                                      size_t wsplit_size, float eps, float *proj, float *r,
-                                      hipStream_t stream);
+                                         hipEvent_t before_k1, hipEvent_t after_k1,
+                                         hipEvent_t after_k2);
 
 /* A static, human-readable name for a status code. */
 const char *mhcpb_status_string(mhcpb_status_t status);

@@ -41,7 +41,6 @@ EXPORTED = (
     "mhcpb_plan_split_count", "mhcpb_execute", "mhcpb_execute_with_events",
     "mhcpb_execute_dx", "mhcpb_execute_dw", "mhcpb_status_string",
     "mhcpb_forward_workspace_bytes", "mhcpb_forward", "mhcpb_forward_with_events",
-    "mhcpb_forward_prepare_weight", "mhcpb_forward_prepared",
 )
 
 _vp = ctypes.c_void_p
@@ -70,11 +69,6 @@ _lib.mhcpb_forward.argtypes = _FWD_ARGS
 _lib.mhcpb_forward.restype = ctypes.c_int
 _lib.mhcpb_forward_with_events.argtypes = _FWD_ARGS + [_vp, _vp, _vp]
 _lib.mhcpb_forward_with_events.restype = ctypes.c_int
-_lib.mhcpb_forward_prepare_weight.argtypes = [_vp, _vp, _vp, ctypes.c_size_t, _vp]
-_lib.mhcpb_forward_prepare_weight.restype = ctypes.c_int
-_lib.mhcpb_forward_prepared.argtypes = [_vp, _vp, _vp, ctypes.c_size_t, ctypes.c_float, _vp,
-                                        _vp, _vp]
-_lib.mhcpb_forward_prepared.restype = ctypes.c_int
 _lib.mhcpb_status_string.argtypes = [ctypes.c_int]
 _lib.mhcpb_status_string.restype = ctypes.c_char_p
 
@@ -192,7 +186,7 @@ def mhcpb_forward_workspace_bytes(plan: int) -> int:
 
 def mhcpb_forward(plan, x, w, eps: float, proj, r, workspace, workspace_size: int,
                   stream: int = 0, check: bool = True) -> int:
-    """Enqueue the forward map (weight split, then the pass over X)."""
+    """Enqueue the forward map (pass over X, then the sum of the tiles)."""
     st = _lib.mhcpb_forward(plan, _ptr(x), _ptr(w), float(eps), _ptr(proj), _ptr(r),
                             _ptr(workspace), int(workspace_size), stream)
     if check and st != MHCPB_SUCCESS:
@@ -201,31 +195,13 @@ def mhcpb_forward(plan, x, w, eps: float, proj, r, workspace, workspace_size: in
 
 
 def mhcpb_forward_with_events(plan, x, w, eps: float, proj, r, workspace, workspace_size: int,
-                              stream: int, before_split: int | None, before_pass: int | None,
-                              after_pass: int | None, check: bool = True) -> int:
-    """mhcpb_forward with caller-owned hipEvent_t handles on the dispatches."""
+                              stream: int, before_k1: int | None, after_k1: int | None,
+                              after_k2: int | None, check: bool = True) -> int:
+    """mhcpb_forward with caller-owned hipEvent_t handles on the dispatches
+    (start and end of kernel 1, end of kernel 2)."""
     st = _lib.mhcpb_forward_with_events(plan, _ptr(x), _ptr(w), float(eps), _ptr(proj),
                                         _ptr(r), _ptr(workspace), int(workspace_size), stream,
-                                        before_split, before_pass, after_pass)
+                                        before_k1, after_k1, after_k2)
     if check and st != MHCPB_SUCCESS:
         raise MhcpbError(st, "mhcpb_forward_with_events")
-    return st
-
-
-def mhcpb_forward_prepare_weight(plan, w, wsplit, wsplit_size: int, stream: int = 0,
-                                 check: bool = True) -> int:
-    """Write the TF32 split of W (two BF16 planes) into wsplit."""
-    st = _lib.mhcpb_forward_prepare_weight(plan, _ptr(w), _ptr(wsplit), int(wsplit_size), stream)
-    if check and st != MHCPB_SUCCESS:
-        raise MhcpbError(st, "mhcpb_forward_prepare_weight")
-    return st
-
-
-def mhcpb_forward_prepared(plan, x, wsplit, wsplit_size: int, eps: float, proj, r,
-                           stream: int = 0, check: bool = True) -> int:
-    """The pass over X with a weight split prepared earlier."""
-    st = _lib.mhcpb_forward_prepared(plan, _ptr(x), _ptr(wsplit), int(wsplit_size), float(eps),
-                                     _ptr(proj), _ptr(r), stream)
-    if check and st != MHCPB_SUCCESS:
-        raise MhcpbError(st, "mhcpb_forward_prepared")
     return st

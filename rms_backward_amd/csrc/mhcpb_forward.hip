@@ -6,48 +6,48 @@
 // prime-kernels pull request 15 page lists the RMS and the gate logits of the
 // streams as one pass, "mhc_projection").
 //
-// Kernel "split_weight": W [24, K] FP32 -> the high part of TF32(W) (its
-// upper 16 bits) and the exact low part as BF16, laid out in the order the
-// main kernel's lanes load them, so that it spends no arithmetic on W and
-// reads it in whole cache lines.  It takes the caller's workspace, zero past
-// K up to a whole number of 64-column chunks.
-//
-// Kernel "forward_kernel": one workgroup per 16 tokens.  Its NW waves split
-// the K columns into 64-column chunks (wave w takes chunks w, w + NW, ...),
-// so each wave walks the whole row block once and keeps the 16 x 24 logits
-// of its columns in MFMA accumulators; at the end the waves' partial sums are
-// added in wave order through LDS.  The order of every sum depends on K and
-// NW only, so a row's result does not depend on T or on the other rows.
+// Kernel 1 ("forward_tiles").  The K columns are cut into tiles of 1024 and
+// the tokens into steps of 16; a unit of work is (tile, step).  Workgroup b
+// takes a contiguous run of units, tile-major, so one round of workgroups
+// covers any T.  Each of its 8 waves owns 128 columns of the tile and keeps
+// their W, split into BF16 high and low parts, in registers for as long as
+// the tile lasts: W is read once per workgroup and tile instead of once per
+// token block.  A wave streams its 16 x 128 block of each unit from HBM into
+// a three-stage LDS ring by LDS DMA, 64 columns a step, two steps ahead (one
+// DMA instruction moves 8 rows x 128 contiguous bytes; the 16-byte segments
+// of a row are XOR-swizzled so that the A-operand reads, 16 tokens at one
+// segment, hit 16 different bank groups).  It forms the 16 x 24 logits of its
+// columns on the MFMA and the sums of squares of its x; the 8 waves' results
+// are added in wave order through LDS slots, each wave reducing two of the
+// 16 tokens, and the tile's partial logits and sums of squares go to the
+// workspace.  Kernel 2 ("forward_reduce") adds the tiles' partials of each
+// token in tile order and computes r.  Every sum has an order fixed by K
+// alone, so a row's result does not depend on T, on the other rows or on the
+// launch shape.
 //
 // Products.  TF32(x) = xh + xl exactly, with xh the upper 16 bits of the TF32
 // value and xl the (at most 3-bit) remainder, both BF16; likewise for W.  On
 // v_mfma_f32_16x16x32_bf16 (A = 16 tokens x 32 columns, B = 32 columns x 16
-// gates) lane l supplies token / gate l % 16 and columns 8 (l / 16) .. +7 of a
-// 32-column group.  Gates 0..15 take four MFMAs per group (xh wh, xh wl, xl
-// wh, xl wl); gates 16..23 take two, with B lanes 0..7 holding wh and lanes
-// 8..15 wl of the same gates, so their logits are the sum of two accumulator
-// columns at the end.  Every BF16 product is exact and the MFMA adds in FP32.
-//
-// Memory.  X streams from HBM into a three-stage LDS ring per wave by LDS DMA
-// (buffer_load_dwordx4 ... lds, non-temporal), two chunks ahead of the one
-// being computed, at no register cost.  One DMA instruction moves 8 rows x 128
-// contiguous bytes; the 16-byte segments of a row are XOR-swizzled so that the
-// A-operand reads (16 tokens at one segment) hit 16 different bank groups.
-// W (read by every workgroup, L2-resident) is stored by split_weight in the
-// order of the MFMA operands, so each W load of a wave is 1 KB of
-// consecutive bytes, and is loaded into registers one chunk ahead.  Rows past T
-// fall outside the X buffer range, the columns past K of a ragged last chunk
-// take offsets outside it, and both read as zeros.
+// gates) lane l supplies token / gate l % 16 and eight columns of a 32-column
+// group: 8q .. 8q + 7 (q = l / 16; A and B agree).
+// Gates 0..15 take four MFMAs per group (xh wh, xh wl, xl wh, xl wl); gates
+// 16..23 take two, with B lanes 0..7 holding wh and lanes 8..15 wl of the
+// same gates, so their logits are the sum of two accumulator columns.  Every
+// BF16 product is exact and the MFMA adds in FP32.
+#include <cstddef>
+
 #include "mhcpb_device.h"
 #include "mhcpb_internal.h"
 
 namespace mhcpb {
 namespace {
 
-constexpr int kFwdRows = 16;    // tokens per workgroup
-constexpr int kFwdChunk = 64;   // columns per step
-constexpr int kFwdDma = 4;      // LDS DMA instructions per step (16 rows x 256 bytes)
-constexpr int kFwdWLoads = 6;   // 16-byte W loads per lane per step
+constexpr int kFwdRows = 16;                 // tokens per unit
+constexpr int kFwdPairs = kFwdRows / 2;      // partial blocks (two tokens each) per unit
+constexpr int kFwdStepCols = 64;             // columns per step (2 MFMA groups)
+constexpr int kFwdDma = 4;                   // LDS DMA instructions per step
+constexpr int kFwdStages = 3;                // LDS ring stages per wave
+constexpr int kFwdSlots = 3;                 // LDS reduction slots in rotation
 
 // Cache policy of the X stream (read once): non-temporal.
 #ifndef MHCPB_FWD_X_AUX
@@ -56,44 +56,16 @@ constexpr int kFwdWLoads = 6;   // 16-byte W loads per lane per step
 
 // TF32 value of v as bits: nearest even at 10 fraction bits, the carry
 // running into the exponent.  A NaN whose top fraction bits are all ones can
-// carry out of the exponent here; the caller repairs such rows afterwards
-// (their RMS is NaN).
+// carry out of the exponent here; kernel 2 repairs such rows (their RMS is
+// NaN).
 __device__ __forceinline__ uint32_t tf32_bits(float v) {
     const uint32_t u = __float_as_uint(v);
     return (u + 0xFFFu + ((u >> 13) & 1u)) & 0xFFFFE000u;
 }
 
-// The four words of a raw buffer resource over [base, base + bytes).
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 rsrc_words(const void *base, int bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a))),
-                 __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu)),
-                 __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3};
-}
-
-// A 16-byte buffer load that the compiler does not track.  Its caller waits
-// for it with an asm wait that names the destination register, in the same
-// basic block: between the two the register holds no value the compiler
-// knows of, and nothing may copy it.  (A tracked load would make the compiler
-// insert its own waits, which do not count the X DMA at the loop head and so
-// would drain the X stream.)
-__device__ __forceinline__ u32x4 load_b128_untracked(i32x4 rs, uint32_t off) {
-    u32x4 v;
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rs));
-    return v;
-}
-
-// Waits until at most N vector memory requests are outstanding; names the
-// six W registers of a step, so their values count as produced here.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_w(const u32x4 (&wv)[6]) {
-    asm volatile("s_waitcnt vmcnt(%6)"
-                 : "+v"(const_cast<u32x4 &>(wv[0])), "+v"(const_cast<u32x4 &>(wv[1])),
-                   "+v"(const_cast<u32x4 &>(wv[2])), "+v"(const_cast<u32x4 &>(wv[3])),
-                   "+v"(const_cast<u32x4 &>(wv[4])), "+v"(const_cast<u32x4 &>(wv[5]))
-                 : "n"(N)
-                 : "memory");
+// A buffer offset, moved outside every range unless `in` holds.
+__device__ __forceinline__ uint32_t offset_if(bool in, uint32_t off) {
+    return in ? off : kOutOfRange;
 }
 
 // Lower halves of two 32-bit words: (a & 0xFFFF) | (b << 16).
@@ -101,273 +73,492 @@ __device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 
-// W [24, K] -> its TF32 split in the order the MFMA B operands are loaded:
-// for chunk c (64 columns), operand e = 3G + kind (G: column group of 32,
-// kind 0 = high parts of gates 0..15, 1 = low parts of gates 0..15, 2 = high
-// parts of gates 16..23 in lanes n < 8 and low parts in lanes n >= 8) and
-// lane l = 16q + n, the 16 bytes wtile[c][e][l] hold the eight BF16 parts of
-// that gate at columns 64c + 32G + 8q .. +7.  One W load of a wave is then
-// 1 KB of consecutive bytes.  Columns past K are zero, so a partial last
-// chunk needs no mask on the W side.  One 16-byte fragment per thread (K is
-// a multiple of 8, so its eight columns are all inside or all padding).
-// Non-finite W keeps its class in the high part (NaN as the quiet NaN) with
-// a zero low part.
-__global__ __launch_bounds__(256) void split_weight(const float *__restrict__ w,
-                                                    u32x4 *__restrict__ wtile, int64_t K,
-                                                    int64_t nfrag) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= nfrag) return;
-    const int lane = static_cast<int>(i % kWave);
-    const int e = static_cast<int>((i / kWave) % kFwdWLoads);
-    const int64_t c = i / (kWave * kFwdWLoads);
-    const int q = lane / 16, n = lane % 16;
-    const int G = e / 3, kind = e % 3;
-    const int gate = kind < 2 ? n : 16 + (n & 7);
-    const bool low = kind == 1 || (kind == 2 && n >= 8);
-    const int64_t col = kFwdChunk * c + 32 * G + 8 * q;
-    u32x4 out = {0u, 0u, 0u, 0u};
-    if (col < K) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(w + gate * K + col);
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(w + gate * K + col + 4);
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t pk[8];  // hi | lo << 16
-#pragma unroll
-        for (int k = 0; k < 8; ++k) pk[k] = tf32_split_packed(v[k]);
-        out = low ? u32x4{hi_halves(pk[0], pk[1]), hi_halves(pk[2], pk[3]),
-                          hi_halves(pk[4], pk[5]), hi_halves(pk[6], pk[7])}
-                  : u32x4{lo_halves(pk[0], pk[1]), lo_halves(pk[2], pk[3]),
-                          lo_halves(pk[4], pk[5]), lo_halves(pk[6], pk[7])};
-    }
-    wtile[i] = out;
+// One reduction slot: each wave's 16 x 32 accumulator block in MFMA output
+// layout (acc[w][b][lane] holds rows 4 (lane / 16) + i, column 16 b + lane %
+// 16, i = 0..3) and the sums of squares of its 16 tokens.
+template <int NW>
+struct FwdSlot {
+    f32x4 acc[NW][2][kWave];
+    float ss[NW][kFwdRows];
+};
+
+// Untracked vector memory: the kernel counts its own requests (LDS DMA of
+// X, W loads, partial stores) in explicit vmcnt waits, so none of them may
+// make the compiler insert a wait of its own, which would not count the DMA
+// and would drain the X stream.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a))),
+                 __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu)),
+                 __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3};
+}
+// The destination register holds no value the compiler knows of until a
+// wait that names it, in the same basic block, has passed.
+__device__ __forceinline__ f32x4 load_b128_untracked(i32x4 rs, uint32_t off) {
+    f32x4 v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rs));
+    return v;
+}
+__device__ __forceinline__ void store_b32_untracked(i32x4 rs, uint32_t off, float v) {
+    asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(v), "v"(off), "s"(rs) : "memory");
 }
 
-template <int NW, int NS>
-__global__ __launch_bounds__(NW * kWave) void forward_kernel(
-    const float *__restrict__ x, const uint16_t *__restrict__ wsplit, float *__restrict__ proj,
-    float *__restrict__ rout, int64_t T, int64_t K, float eps) {
-    static_assert(NS >= 3, "X is requested at least two chunks ahead");
-    constexpr int DX = NS - 1;  // chunks of X requested ahead of the one computed
-    __shared__ f32x4 xring[NW][NS][kFwdDma][kWave];
-    static_assert(sizeof(xring) >= NW * kWave * (2 * 16 + 4), "reduction area fits the ring");
-    const int lane = threadIdx.x % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int q = lane / 16;
-    const int n16 = lane % 16;
-    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kFwdRows;
-    const int rows = static_cast<int>((T - row0) < kFwdRows ? (T - row0) : kFwdRows);
-    const int ki = static_cast<int>(K);  // K <= 2^22
-    const int nchunks = (ki + kFwdChunk - 1) / kFwdChunk;
-    const int nsteps = wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;
+// What one wave of forward_tiles knows of its work (all uniform but the
+// lane fields).
+struct FwdCtx {
+    const float *x;
+    const float *w;
+    float *part;
+    int64_t T;
+    int ki;       // K (<= 2^22)
+    int nsteps;   // 16-token steps of T
+    int u_begin;
+    int nu;       // units of this workgroup
+    int wcols;    // columns per wave
+    int wave;
+    int lane, q, n16;
+    uint32_t ring;   // LDS address of this wave's X ring
+    uint32_t slots;  // LDS address of the reduction slots
+    uint32_t ready, consumed;
+};
 
-    // LDS DMA: instruction rr = 2a + b of a step moves rows 8a .. 8a+7 and
-    // segments 8b .. 8b+7 (16 bytes = 4 columns each) of the chunk; lane L
-    // fetches row 8a + L/8, segment 8b + ((L % 8) ^ (L/8) ^ a), which lands at
-    // LDS position 64 rr + L (16-byte units) of the stage.
-    // The last chunk of a ragged K masks the columns past K (their offsets
-    // move outside every range); chunks past the end get an empty range.
-    const int tail0 = kFwdChunk * (nchunks - 1);
-    uint32_t xoff[kFwdDma], xoff_tail[kFwdDma];
+// A unit of the workgroup's run: tile kt, 16-token step s (first token
+// 16 s), its rows (16, or fewer at the end of T), and whether it lies in the
+// run.  Uniform; advanced one unit at a time without divisions.
+struct FwdUnit {
+    int kt;
+    int s;
+    int rows;
+    bool valid;
+};
+__device__ __forceinline__ FwdUnit fwd_unit_at(const FwdCtx &c, int s, int kt, int i) {
+    FwdUnit r;
+    r.kt = kt;
+    r.s = s;
+    const int64_t left = c.T - static_cast<int64_t>(s) * kFwdRows;
+    r.rows = static_cast<int>(left < kFwdRows ? left : kFwdRows);
+    r.valid = i < c.nu;
+    return r;
+}
+__device__ __forceinline__ FwdUnit fwd_first(const FwdCtx &c) {
+    return fwd_unit_at(c, c.u_begin % c.nsteps, c.u_begin / c.nsteps, 0);
+}
+// The unit after un, which is unit i of the run.
+__device__ __forceinline__ FwdUnit fwd_next(const FwdCtx &c, const FwdUnit &un, int i) {
+    const bool wrap = un.s + 1 == c.nsteps;
+    return fwd_unit_at(c, wrap ? 0 : un.s + 1, wrap ? un.kt + 1 : un.kt, i);
+}
+__device__ __forceinline__ int fwd_colbase(const FwdCtx &c, int kt) {
+    return __builtin_amdgcn_readfirstlane(kt * kFwdTileCols + c.wave * c.wcols);
+}
+
+// Step h of unit un (64 columns) into the ring stage at LDS address `stage`
+// by 4 LDS DMA: instruction rr = 2a + b moves rows 8a .. 8a+7 and 16-byte
+// segments 8b .. 8b+7 of the 64 columns; lane L fetches row 8a + L/8,
+// segment 8b + ((L % 8) ^ (L/8) ^ a), which lands at LDS position 64 rr + L
+// (16-byte units) of the stage.  Units past the workgroup's run get an empty
+// range, rows past T fall outside the range, and columns past K take
+// out-of-range offsets; all of them read zeros.
+__device__ __forceinline__ void fwd_issue_x(const FwdCtx &c, const FwdUnit &un, int h,
+                                            uint32_t stage, const uint32_t (&xoff)[kFwdDma],
+                                            const int (&xcol)[kFwdDma]) {
+    const int col0 = fwd_colbase(c, un.kt) + kFwdStepCols * h;
+    const int n = un.valid ? un.rows * c.ki - col0 : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc32(c.x + static_cast<int64_t>(un.s) * kFwdRows * c.ki + col0,
+                    __builtin_amdgcn_readfirstlane(n > 0 ? n : 0) * 4);
+    const int lim = c.ki - col0;
+#pragma unroll
+    for (int rr = 0; rr < kFwdDma; ++rr)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (MHCPB_LDS void *)(static_cast<uintptr_t>(stage + rr * kWave * 16)), 16,
+            offset_if(xcol[rr] < lim, xoff[rr]), 0, 0, MHCPB_FWD_X_AUX);
+}
+
+// The B operands of tile kt for this wave: per group G, [0] high parts of
+// gate n16, [1] its low parts, [2] the high (n16 < 8) or low (n16 >= 8)
+// parts of gate 16 + n16 % 8, at columns 32G + 8q .. + 7 of the wave's
+// columns; columns past K are zero.  Waits for every request of the wave (a
+// tile change is rare).
+template <int NG>
+__device__ __forceinline__ void fwd_load_w(const FwdCtx &c, int kt, u32x4 (&bw)[NG][3]) {
+    const int colbase = fwd_colbase(c, kt);
+    const i32x4 rs = rsrc_words(c.w, kProjCols * c.ki * 4);
+    const int g1 = 16 + (c.n16 & 7);
+#pragma unroll
+    for (int G0 = 0; G0 < NG; G0 += 4) {  // four groups (16 loads) per wait
+        f32x4 v0[4][2], v1[4][2];
+#pragma unroll
+        for (int G = 0; G < 4; ++G)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int col = colbase + 32 * (G0 + G) + 8 * c.q + 4 * h;
+                const bool in = col < c.ki;
+                v0[G][h] = load_b128_untracked(
+                    rs, offset_if(in, static_cast<uint32_t>((c.n16 * c.ki + col) * 4)));
+                v1[G][h] = load_b128_untracked(
+                    rs, offset_if(in, static_cast<uint32_t>((g1 * c.ki + col) * 4)));
+            }
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(v0[0][0]), "+v"(v0[0][1]), "+v"(v0[1][0]), "+v"(v0[1][1]),
+                       "+v"(v0[2][0]), "+v"(v0[2][1]), "+v"(v0[3][0]), "+v"(v0[3][1]),
+                       "+v"(v1[0][0]), "+v"(v1[0][1]), "+v"(v1[1][0]), "+v"(v1[1][1]),
+                       "+v"(v1[2][0]), "+v"(v1[2][1]), "+v"(v1[3][0]), "+v"(v1[3][1])::"memory");
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+            uint32_t p0[8], p1[8];  // hi | lo << 16
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p0[e] = tf32_split_packed(v0[G][e / 4][e % 4]);
+                p1[e] = tf32_split_packed(v1[G][e / 4][e % 4]);
+            }
+            bw[G0 + G][0] = u32x4{lo_halves(p0[0], p0[1]), lo_halves(p0[2], p0[3]),
+                                  lo_halves(p0[4], p0[5]), lo_halves(p0[6], p0[7])};
+            bw[G0 + G][1] = u32x4{hi_halves(p0[0], p0[1]), hi_halves(p0[2], p0[3]),
+                                  hi_halves(p0[4], p0[5]), hi_halves(p0[6], p0[7])};
+            bw[G0 + G][2] = c.n16 < 8 ? u32x4{lo_halves(p1[0], p1[1]), lo_halves(p1[2], p1[3]),
+                                              lo_halves(p1[4], p1[5]), lo_halves(p1[6], p1[7])}
+                                      : u32x4{hi_halves(p1[0], p1[1]), hi_halves(p1[2], p1[3]),
+                                              hi_halves(p1[4], p1[5]), hi_halves(p1[6], p1[7])};
+        }
+    }
+}
+
+// LDS addresses within a slot (FwdSlot<NW> layout).
+template <int NW>
+__device__ __forceinline__ uint32_t fwd_slot_acc(const FwdCtx &c, int slot, int w, int b, int l) {
+    return c.slots + static_cast<uint32_t>(slot * sizeof(FwdSlot<NW>) +
+                                           ((w * 2 + b) * kWave + l) * sizeof(f32x4));
+}
+template <int NW>
+__device__ __forceinline__ uint32_t fwd_slot_ss(const FwdCtx &c, int slot, int w, int m) {
+    return c.slots + static_cast<uint32_t>(slot * sizeof(FwdSlot<NW>) +
+                                           offsetof(FwdSlot<NW>, ss) + (w * kFwdRows + m) * 4);
+}
+
+// Reduction of unit i by this wave: token pairs p = wave (8 / NW) + j, one
+// pair per pass; lane L takes token 2p + L / 32, column L % 32 of the
+// 32-wide rows (0..15 gates 0..15, 16..23 high parts and 24..31 low parts of
+// gates 16..23), and the lanes of column 24 also sum the squares.  Waits
+// until every wave has written unit i, adds the NW waves in order, frees the
+// slot and writes block (tile, step, p) of the workspace: 64 floats in lane
+// order, token 2p + h at floats 32 h .. 32 h + 31 (logits 0..23, the squares
+// at 24, zeros after), one store per pair.  For i < 0 the stores go to an
+// empty range: every unit issues the same requests.
+template <int NW>
+__device__ __forceinline__ void fwd_reduce(const FwdCtx &c, int i, const FwdUnit &un) {
+    constexpr int kPairsPerWave = kFwdPairs / NW;
+    const int col = c.lane % 32;
+    float sum[kPairsPerWave], ssum[kPairsPerWave];
+#pragma unroll
+    for (int j = 0; j < kPairsPerWave; ++j) sum[j] = ssum[j] = 0.f;
+    if (i >= 0) {
+        const int slot = i % kFwdSlots;
+        lds_wait_at_least(c.ready + 4 * slot, NW * static_cast<uint32_t>(i / kFwdSlots + 1));
+        const int b = col / 16, nn = col % 16;
+        float v[kPairsPerWave][NW], sv[kPairsPerWave][NW];
+#pragma unroll
+        for (int j = 0; j < kPairsPerWave; ++j) {
+            const int m = 2 * (c.wave * kPairsPerWave + j) + c.lane / 32;
+            const uint32_t src = fwd_slot_acc<NW>(c, slot, 0, b, 16 * (m / 4) + nn) + 4 * (m % 4);
+            const uint32_t ssrc = fwd_slot_ss<NW>(c, slot, 0, m);
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                v[j][ww] = lds_read_f32(src + ww * (2 * kWave * 16));
+                sv[j][ww] = lds_read_f32(ssrc + ww * (kFwdRows * 4));
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < kPairsPerWave; ++j)
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww)
+                asm volatile("" : "+v"(v[j][ww]), "+v"(sv[j][ww]));
+        lds_signal(c.consumed + 4 * slot, c.lane);
+#pragma unroll
+        for (int j = 0; j < kPairsPerWave; ++j) {
+            sum[j] = v[j][0];
+            ssum[j] = sv[j][0];
+#pragma unroll
+            for (int ww = 1; ww < NW; ++ww) {
+                sum[j] += v[j][ww];
+                ssum[j] += sv[j][ww];
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kPairsPerWave; ++j) {
+        const float low = __shfl_xor(sum[j], 8);  // column + 8: the low part
+        if (col >= 16 && col < 24) sum[j] += low;
+        const float out = col < kProjCols ? sum[j] : (col == kProjCols ? ssum[j] : 0.f);
+        const int p = c.wave * kPairsPerWave + j;
+        const int64_t blk = (static_cast<int64_t>(un.kt) * c.nsteps + un.s) * kFwdPairs + p;
+        const i32x4 brs = rsrc_words(c.part + blk * kWave, i >= 0 ? kWave * 4 : 0);
+        store_b32_untracked(brs, static_cast<uint32_t>(c.lane * 4), out);
+    }
+}
+
+// Step h of unit i (groups 2h, 2h + 1 of the wave's W), read from ring stage
+// sb; requests step (h + 2) of the same unit or step h + 2 - SPU of the next
+// (two steps ahead) into stage sb_next.  Requests: 4 DMA per step, and at the
+// end of each unit the NW-dependent partial stores (kStores) of the
+// reduction of the previous unit.  At the top of step h the requests after
+// its X are the next step's 4 DMA, plus the stores when a unit's end lies
+// between (h < 2): the wait leaves exactly those in flight.  `first` marks
+// the first unit, before which no stores were issued.
+template <int NW, int NG, int H>
+__device__ __forceinline__ void fwd_step(const FwdCtx &c, bool first, uint32_t sb, uint32_t sb_next,
+                                         const FwdUnit &pre, const uint32_t (&xoff)[kFwdDma],
+                                         const int (&xcol)[kFwdDma], const uint32_t (&rd)[2][2],
+                                         const u32x4 (&bw)[NG][3], f32x4 &acc0, f32x4 &acc1,
+                                         float &ss) {
+    constexpr int SPU = NG / 2;
+    constexpr int kStores = kFwdPairs / NW;
+    if (H >= 2 || first)
+        wait_vmcnt<kFwdDma>();
+    else
+        wait_vmcnt<kFwdDma + kStores>();
+    f32x4 xv[2][2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) xv[G][h] = lds_read_b128(sb + rd[G][h]);
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(xv[0][0]), "+v"(xv[0][1]), "+v"(xv[1][0]), "+v"(xv[1][1])::"memory");
+    compiler_fence();
+    fwd_issue_x(c, pre, (H + 2) % SPU, sb_next, xoff, xcol);
+    compiler_fence();
+#pragma unroll
+    for (int G2 = 0; G2 < 2; ++G2) {
+        const int G = 2 * H + G2;
+        const float v[8] = {xv[G2][0].x, xv[G2][0].y, xv[G2][0].z, xv[G2][0].w,
+                            xv[G2][1].x, xv[G2][1].y, xv[G2][1].z, xv[G2][1].w};
+        uint32_t tv[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            tv[e] = tf32_bits(v[e]);
+            lo[e] = __float_as_uint(__uint_as_float(tv[e]) - __uint_as_float(tv[e] & 0xFFFF0000u));
+        }
+        const u32x4 ahi = {hi_halves(tv[0], tv[1]), hi_halves(tv[2], tv[3]),
+                           hi_halves(tv[4], tv[5]), hi_halves(tv[6], tv[7])};
+        const u32x4 alo = {hi_halves(lo[0], lo[1]), hi_halves(lo[2], lo[3]),
+                           hi_halves(lo[4], lo[5]), hi_halves(lo[6], lo[7])};
+        acc0 = mfma(ahi, bw[G][0], acc0);
+        acc0 = mfma(ahi, bw[G][1], acc0);
+        acc0 = mfma(alo, bw[G][0], acc0);
+        acc0 = mfma(alo, bw[G][1], acc0);
+        acc1 = mfma(ahi, bw[G][2], acc1);
+        acc1 = mfma(alo, bw[G][2], acc1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
+    }
+}
+
+// The steps of one unit, H = 0 .. SPU - 1; stage indices cycle through 3.
+template <int NW, int NG, int H>
+__device__ __forceinline__ void fwd_steps(const FwdCtx &c, bool first, int &stage,
+                                          const FwdUnit &cur, const FwdUnit &nxt,
+                                          const uint32_t (&xoff)[kFwdDma], const int (&xcol)[kFwdDma],
+                                          const uint32_t (&rd)[2][2], const u32x4 (&bw)[NG][3],
+                                          f32x4 &acc0, f32x4 &acc1, float &ss) {
+    if constexpr (H < NG / 2) {
+        constexpr uint32_t kStage = kFwdDma * kWave * 16;
+        const int s1 = stage == 2 ? 0 : stage + 1;
+        const int s2 = s1 == 2 ? 0 : s1 + 1;  // stage of the step two ahead
+        fwd_step<NW, NG, H>(c, first, c.ring + stage * kStage, c.ring + s2 * kStage,
+                            H + 2 < NG / 2 ? cur : nxt, xoff, xcol, rd, bw, acc0, acc1, ss);
+        stage = s1;
+        fwd_steps<NW, NG, H + 1>(c, first, stage, cur, nxt, xoff, xcol, rd, bw, acc0, acc1, ss);
+    }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void forward_tiles(
+    const float *__restrict__ x, const float *__restrict__ w, float *__restrict__ part, int64_t T,
+    int64_t K, int units, int upw, int nsteps) {
+    constexpr int NG = kFwdTileCols / (32 * NW);  // 32-column groups per wave
+    constexpr int SPU = NG / 2;                   // steps per unit
+    static_assert(NG % 2 == 0 && SPU >= 2, "at least two steps per unit");
+    __shared__ f32x4 xring[NW][kFwdStages][kFwdDma][kWave];
+    __shared__ FwdSlot<NW> slots[kFwdSlots];
+    __shared__ uint32_t ready[kFwdSlots], consumed[kFwdSlots];
+    FwdCtx c;
+    c.x = x;
+    c.w = w;
+    c.part = part;
+    c.T = T;
+    c.ki = static_cast<int>(K);
+    c.nsteps = nsteps;
+    c.u_begin = static_cast<int>(blockIdx.x) * upw;
+    c.nu = (c.u_begin + upw < units ? c.u_begin + upw : units) - c.u_begin;
+    c.wcols = NG * 32;
+    c.lane = threadIdx.x % kWave;
+    c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    c.q = c.lane / 16;
+    c.n16 = c.lane % 16;
+    c.ring = lds_addr(&xring[c.wave][0][0][0]);
+    c.slots = lds_addr(&slots[0]);
+    c.ready = lds_addr(&ready[0]);
+    c.consumed = lds_addr(&consumed[0]);
+    if (threadIdx.x < kFwdSlots) {
+        lds_write_u32(c.ready + 4 * threadIdx.x, 0u);
+        lds_write_u32(c.consumed + 4 * threadIdx.x, 0u);
+    }
+    lds_barrier();
+
+    // DMA offsets of this lane (see fwd_issue_x) and the A-operand reads:
+    // lane (q, token m) reads segments 8G + 2q + h (h = 0, 1) of column group
+    // G of the step; their positions in a stage follow from the DMA map.
+    uint32_t xoff[kFwdDma];
+    int xcol[kFwdDma];
 #pragma unroll
     for (int rr = 0; rr < kFwdDma; ++rr) {
-        const int a = rr >> 1, b = rr & 1, mi = lane >> 3;
-        const int seg = 8 * b + ((lane & 7) ^ mi ^ a);
-        xoff[rr] = static_cast<uint32_t>(((8 * a + mi) * ki + 4 * seg) * 4);
-        xoff_tail[rr] = tail0 + 4 * seg < ki ? xoff[rr] : kOutOfRange;
+        const int a = rr >> 1, b = rr & 1, mi = c.lane >> 3;
+        const int seg = 8 * b + ((c.lane & 7) ^ mi ^ a);
+        xcol[rr] = 4 * seg;
+        xoff[rr] = static_cast<uint32_t>(((8 * a + mi) * c.ki + 4 * seg) * 4);
     }
-    // A-operand reads: lane (q, token m) reads segments 8G + 2q + h (h = 0, 1)
-    // of column group G; their positions in a stage follow from the DMA map.
     uint32_t rd[2][2];
     {
-        const int a = n16 >> 3, mi = n16 & 7;
+        const int a = c.n16 >> 3, mi = c.n16 & 7;
 #pragma unroll
         for (int G = 0; G < 2; ++G)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int si = 2 * q + h;
+                const int si = 2 * c.q + h;
                 rd[G][h] = static_cast<uint32_t>((64 * (2 * a + G) + 8 * mi + (si ^ mi ^ a)) * 16);
             }
     }
-    // W: B operand e of chunk c for this lane is the 16 bytes at
-    // ((6c + e) 64 + lane) 16 of the tiled split (see split_weight).
-    uint32_t woff[kFwdWLoads];
-#pragma unroll
-    for (int e = 0; e < kFwdWLoads; ++e) woff[e] = static_cast<uint32_t>((e * kWave + lane) * 16);
 
-    const uint32_t ring = lds_addr(&xring[wave][0][0][0]);
-    constexpr uint32_t kStageBytes = kFwdDma * kWave * 16;
-    // Chunk c of X into ring stage `stage` (4 LDS DMA), and the W of chunk c
-    // (6 loads).  Neither branches: the step's request count stays fixed.
-    auto issue_x = [&](int c, int stage) {
-        const int c0 = kFwdChunk * c;
-        const int n = c < nchunks ? rows * ki - c0 : 0;
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc32(x + row0 * K + c0, __builtin_amdgcn_readfirstlane(n) * 4);
-        const bool tail = c == nchunks - 1;
-#pragma unroll
-        for (int rr = 0; rr < kFwdDma; ++rr)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (MHCPB_LDS void *)(&xring[wave][stage][rr][0]), 16,
-                tail ? xoff_tail[rr] : xoff[rr], 0, 0, MHCPB_FWD_X_AUX);
-    };
-    auto load_w = [&](int c, u32x4 (&wv)[kFwdWLoads]) {
-        const int n = c < nchunks ? kFwdWLoads * kWave * 16 : 0;
-        const i32x4 rs = rsrc_words(wsplit + static_cast<int64_t>(c) * (kFwdWLoads * kWave * 8), n);
-#pragma unroll
-        for (int e = 0; e < kFwdWLoads; ++e) wv[e] = load_b128_untracked(rs, woff[e]);
-    };
+    u32x4 bw[NG][3];
+    FwdUnit cur = fwd_first(c);
+    FwdUnit nxt = fwd_next(c, cur, 1);
+    FwdUnit prev = cur;
+    int kt_loaded = cur.kt;
+    fwd_load_w<NG>(c, kt_loaded, bw);
+    constexpr uint32_t kStage = kFwdDma * kWave * 16;
+    fwd_issue_x(c, cur, 0, c.ring, xoff, xcol);
+    fwd_issue_x(c, cur, 1, c.ring + kStage, xoff, xcol);
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f};  // gates 0..15
     f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};  // gates 16..23: high part | low part
-    float ss = 0.f;                     // sum of x^2 of token n16, this lane's columns
-
-    // One step: chunk wave + NW j from ring stage j % NS with the W of wcur.
-    // Order of the vector memory requests: W(0), W(1), X(0) .. X(DX - 1)
-    // before the loop, then W(j + 2) (into wload), X(j + DX) in step j.  The
-    // wait at the end of step j must leave X(j + 1) in LDS and W(j + 1) (in
-    // wnext) in registers.  With DX = 2, X(j + 1) is the last request of step
-    // j - 1, so the 10 requests of step j stay in flight; with DX >= 3 W(j + 1)
-    // is the first request of step j - 1, so its 4 X requests and the 10 of
-    // step j stay in flight.  Steps past the last chunk still request (an
-    // empty range: zeros), which keeps every step's count the same.
-    constexpr int kStepWait = DX == 2 ? kFwdWLoads + kFwdDma : kFwdWLoads + 2 * kFwdDma;
-    // The last one or two steps of a wave (after the drain below) request
-    // nothing: their X and W were requested by the steps before them.
-    auto step = [&](int j, const u32x4 (&wcur)[kFwdWLoads], u32x4 (&wload)[kFwdWLoads],
-                    u32x4 (&wnext)[kFwdWLoads], bool prefetch) {
-        const int c = wave + NW * j;
-        const uint32_t sb = ring + static_cast<uint32_t>(j % NS) * kStageBytes;
-        f32x4 xv[2][2];
-#pragma unroll
-        for (int G = 0; G < 2; ++G)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) xv[G][h] = lds_read_b128(sb + rd[G][h]);
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(xv[0][0]), "+v"(xv[0][1]), "+v"(xv[1][0]), "+v"(xv[1][1])::"memory");
-        if (prefetch) {
-            compiler_fence();
-            load_w(c + 2 * NW, wload);
-            issue_x(c + DX * NW, (j + DX) % NS);
-            compiler_fence();
+    float ss = 0.f;                     // squares of token n16, this lane's columns
+    int stage = 0;                      // ring stage of the unit's first step
+    for (int i = 0; i < c.nu; ++i) {
+        if (cur.kt != kt_loaded) {  // a new tile: reload W (its wait drains everything)
+            fwd_load_w<NG>(c, cur.kt, bw);
+            kt_loaded = cur.kt;
         }
-#pragma unroll
-        for (int G = 0; G < 2; ++G) {
-            const float v[8] = {xv[G][0].x, xv[G][0].y, xv[G][0].z, xv[G][0].w,
-                                xv[G][1].x, xv[G][1].y, xv[G][1].z, xv[G][1].w};
-            uint32_t t[8], lo[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                t[e] = tf32_bits(v[e]);
-                lo[e] = __float_as_uint(__uint_as_float(t[e]) - __uint_as_float(t[e] & 0xFFFF0000u));
-            }
-            const u32x4 ahi = {hi_halves(t[0], t[1]), hi_halves(t[2], t[3]),
-                               hi_halves(t[4], t[5]), hi_halves(t[6], t[7])};
-            const u32x4 alo = {hi_halves(lo[0], lo[1]), hi_halves(lo[2], lo[3]),
-                               hi_halves(lo[4], lo[5]), hi_halves(lo[6], lo[7])};
-            acc0 = mfma(ahi, wcur[3 * G + 0], acc0);
-            acc0 = mfma(ahi, wcur[3 * G + 1], acc0);
-            acc0 = mfma(alo, wcur[3 * G + 0], acc0);
-            acc0 = mfma(alo, wcur[3 * G + 1], acc0);
-            acc1 = mfma(ahi, wcur[3 * G + 2], acc1);
-            acc1 = mfma(alo, wcur[3 * G + 2], acc1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
-        }
-        if (prefetch) wait_vmcnt_w<kStepWait>(wnext);
-    };
+        fwd_steps<NW, NG, 0>(c, i == 0, stage, cur, nxt, xoff, xcol, rd, bw, acc0, acc1, ss);
+        // Squares of token n16 over the wave's columns: the four quarters in
+        // order ((q0 + q1) + (q2 + q3)).
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const int slot = i % kFwdSlots;
+        lds_wait_at_least(c.consumed + 4 * slot, NW * static_cast<uint32_t>(i / kFwdSlots));
+        lds_write_u128(fwd_slot_acc<NW>(c, slot, c.wave, 0, c.lane), __builtin_bit_cast(u32x4, acc0));
+        lds_write_u128(fwd_slot_acc<NW>(c, slot, c.wave, 1, c.lane), __builtin_bit_cast(u32x4, acc1));
+        if (c.lane < kFwdRows)
+            lds_write_u32(fwd_slot_ss<NW>(c, slot, c.wave, c.lane), __float_as_uint(ss));
+        lds_signal(c.ready + 4 * slot, c.lane);
+        fwd_reduce<NW>(c, i - 1, prev);
+        acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        ss = 0.f;
+        prev = cur;
+        cur = nxt;
+        nxt = fwd_next(c, nxt, i + 2);
+    }
+    if (c.nu > 0) fwd_reduce<NW>(c, c.nu - 1, prev);
+    // The requests past the run (zeros) and the stores land before the
+    // workgroup's LDS is released.
+    wait_vmcnt<0>();
+}
 
-    // Three W register sets in rotation: step j computes with W(j), while
-    // W(j + 1) may still be arriving and W(j + 2) is requested.
-    u32x4 wa[kFwdWLoads], wb[kFwdWLoads], wc[kFwdWLoads];
-    load_w(wave, wa);
-    load_w(wave + NW, wb);
-    compiler_fence();
+// proj[t] = sum over tiles (in order) of the partial logits, r[t] from the
+// summed squares; columns 24..31 of proj are zero.  A row whose sum of
+// squares is NaN has a NaN in X: its logits are NaN.  Thread (t, e) handles
+// logits 4e .. 4e + 3 of token t for e < 6, and e == 6 r and the zero
+// columns; the tiles' loads are issued before they are added, in tile order.
+// Token t's partial of tile kt is at floats 32 (t % 2) .. of block
+// (kt, t / 16, (t % 16) / 2) (see fwd_reduce).
+constexpr int kFwdReduceBatch = 24;
+__global__ __launch_bounds__(256) void forward_reduce(const float *__restrict__ part,
+                                                      float *__restrict__ proj,
+                                                      float *__restrict__ rout, int64_t T,
+                                                      int nkt, int nsteps, int64_t K, float eps) {
+    constexpr int kParts = kProjCols / 4 + 1;
+    const int64_t id = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t t = id / kParts;
+    const int e = static_cast<int>(id % kParts);
+    if (t >= T) return;
+    const int64_t s = t / kFwdRows;
+    const int m = static_cast<int>(t % kFwdRows);
+    // floats of token t in tile 0; tile kt adds kt * tile_stride
+    const int64_t base = (s * kFwdPairs + m / 2) * kWave + 32 * (m % 2);
+    const int64_t tile_stride = static_cast<int64_t>(nsteps) * kFwdPairs * kWave;
+    float ss = 0.f;
+    for (int k0 = 0; k0 < nkt; k0 += kFwdReduceBatch) {
+        float v[kFwdReduceBatch];
 #pragma unroll
-    for (int k = 0; k < DX; ++k) issue_x(wave + k * NW, k);
-    wait_vmcnt_w<kFwdDma * (DX - 1)>(wa);
-    int j = 0;
-    for (; j + 2 < nsteps; j += 3) {
-        step(j, wa, wc, wb, true);
-        step(j + 1, wb, wa, wc, true);
-        step(j + 2, wc, wb, wa, true);
-    }
-    // Every request of this wave lands here, before the last steps and
-    // before the ring is reused below.  The wait names every W register set:
-    // none may be reused before its last load has landed, and after it no
-    // load is in flight, so the branches below cannot meet one.
-    asm volatile("s_waitcnt vmcnt(0)"
-                 : "+v"(wa[0]), "+v"(wa[1]), "+v"(wa[2]), "+v"(wa[3]), "+v"(wa[4]), "+v"(wa[5]),
-                   "+v"(wb[0]), "+v"(wb[1]), "+v"(wb[2]), "+v"(wb[3]), "+v"(wb[4]), "+v"(wb[5]),
-                   "+v"(wc[0]), "+v"(wc[1]), "+v"(wc[2]), "+v"(wc[3]), "+v"(wc[4]), "+v"(wc[5])
-                 :
-                 : "memory");
-    if (j < nsteps) step(j, wa, wc, wb, false);
-    if (j + 1 < nsteps) step(j + 1, wb, wa, wc, false);
-    __syncthreads();
-
-    // Partial sums of each wave, then their sum in wave order by wave 0.
-    f32x4 *red0 = &xring[0][0][0][0];
-    f32x4 *red1 = red0 + NW * kWave;
-    float *red2 = reinterpret_cast<float *>(red1 + NW * kWave);
-    red0[wave * kWave + lane] = acc0;
-    red1[wave * kWave + lane] = acc1;
-    red2[wave * kWave + lane] = ss;
-    __syncthreads();
-    if (wave != 0) return;
-    f32x4 s0 = red0[lane], s1 = red1[lane];
+        for (int k = 0; k < kFwdReduceBatch; ++k)
+            v[k] = k0 + k < nkt
+                       ? __builtin_nontemporal_load(part + base + (k0 + k) * tile_stride + kProjCols)
+                       : 0.f;
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-        s0 += red0[w * kWave + lane];
-        s1 += red1[w * kWave + lane];
+        for (int k = 0; k < kFwdReduceBatch; ++k)
+            if (k0 + k < nkt) ss = (k0 + k == 0) ? v[k] : ss + v[k];
     }
-    // Lanes 0..15: RMS of token `lane` (waves in order, the four column
-    // quarters of each in order).
-    float st = 0.f;
-    if (lane < kFwdRows) {
-        for (int w = 0; w < NW; ++w)
+    const float rv = __builtin_sqrtf(ss / static_cast<float>(K) + eps);
+    const bool nan_row = rv != rv;
+    f32x4 *out = reinterpret_cast<f32x4 *>(proj + t * kProjStride);
+    if (e == kParts - 1) {
+        out[kProjCols / 4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        out[kProjCols / 4 + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        rout[t] = rv;
+        return;
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < nkt; k0 += kFwdReduceBatch) {
+        f32x4 v[kFwdReduceBatch];
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) st += red2[w * kWave + 16 * qq + lane];
+        for (int k = 0; k < kFwdReduceBatch; ++k)
+            v[k] = k0 + k < nkt ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
+                                      part + base + (k0 + k) * tile_stride) + e)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < kFwdReduceBatch; ++k)
+            if (k0 + k < nkt) acc = (k0 + k == 0) ? v[k] : acc + v[k];
     }
-    const float rv = __builtin_sqrtf(st / static_cast<float>(ki) + eps);
-    // Accumulator lane l holds gate l % 16 of tokens 4 (l / 16) + i.  Gates
-    // 16..23 add the high-part column (this lane) and the low-part column
-    // (lane + 8).  A row whose RMS is NaN has a NaN in X: its logits are NaN.
     const float qnan = __builtin_nanf("");
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * q + i;
-        const float rm = __shfl(rv, m);
-        const float other = __shfl_xor(s1[i], 8);
-        if (m < rows) {
-            float *row = proj + (row0 + m) * kProjStride;
-            const bool nan_row = rm != rm;
-            row[n16] = nan_row ? qnan : s0[i];
-            row[16 + n16] = n16 < 8 ? (nan_row ? qnan : s1[i] + other) : 0.f;
-        }
-    }
-    if (lane < rows) rout[row0 + lane] = rv;
+    out[e] = nan_row ? f32x4{qnan, qnan, qnan, qnan} : acc;
 }
 
 }  // namespace
 
-hipError_t launch_split_weight(const Plan &p, const float *w, uint16_t *wsplit, hipStream_t stream,
-                               hipEvent_t start, hipEvent_t stop) {
-    const int64_t nfrag = forward_padded_cols(p.K) / kFwdChunk * kFwdWLoads * kWave;
-    const unsigned blocks = static_cast<unsigned>((nfrag + 255) / 256);
-    launch(split_weight, dim3(blocks), dim3(256), stream, start, stop, w,
-           reinterpret_cast<u32x4 *>(wsplit), p.K, nfrag);
-    return hipGetLastError();
-}
-
-// Eight waves per workgroup: 96 KB of ring, one workgroup per CU; at
-// T = 4096 the grid is one workgroup per CU on 256 CUs.
-hipError_t launch_forward(const Plan &p, const float *x, const uint16_t *wsplit, float *proj,
-                          float *r, float eps, hipStream_t stream, hipEvent_t start,
-                          hipEvent_t stop) {
-    constexpr int NW = 8;
-    constexpr int NS = 3;
-    const dim3 grid(static_cast<unsigned>((p.T + kFwdRows - 1) / kFwdRows));
-    launch(forward_kernel<NW, NS>, grid, dim3(NW * kWave), stream, start, stop, x, wsplit, proj, r,
-           p.T, p.K, eps);
+// Launch shape, a performance choice only: the partials' sums run in an
+// order fixed by the 1024-column tiles, so every shape gives the same bits.
+#ifndef MHCPB_FWD_WAVES
+#define MHCPB_FWD_WAVES 8
+#endif
+hipError_t launch_forward(const Plan &p, const float *x, const float *w, float *proj, float *r,
+                          float eps, float *ws, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t mid, hipEvent_t stop) {
+    constexpr int NW = MHCPB_FWD_WAVES;
+    // workgroups resident per CU (LDS) times 256 CUs: one round
+    constexpr int kGrid = NW == 8 ? 256 : 512;
+    const int nkt = forward_tile_count(p.K);
+    const int nsteps = static_cast<int>((p.T + kFwdRows - 1) / kFwdRows);
+    const int64_t units64 = static_cast<int64_t>(nkt) * nsteps;
+    const int units = static_cast<int>(units64);  // < 2^31: checked before the launch
+    const int upw = (units + kGrid - 1) / kGrid;
+    const int grid = (units + upw - 1) / upw;
+    launch(forward_tiles<NW>, dim3(grid), dim3(NW * kWave), stream, start, mid, x, w, ws, p.T,
+           p.K, units, upw, nsteps);
+    const unsigned blocks = static_cast<unsigned>((p.T * (kProjCols / 4 + 1) + 255) / 256);
+    launch(forward_reduce, dim3(blocks), dim3(256), stream, nullptr, stop, ws, proj, r, p.T, nkt,
+           nsteps, p.K, eps);
     return hipGetLastError();
 }
 

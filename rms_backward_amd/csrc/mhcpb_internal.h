@@ -55,20 +55,32 @@ hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStrea
 // takes the end time of the dispatch.
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop);
 
-// Columns of a row of the forward's weight planes: K rounded up to whole
-// 64-column chunks (the padding is zero).
-inline int64_t forward_padded_cols(int64_t K) { return (K + 63) / 64 * 64; }
+// Forward: the K columns are cut into tiles of kFwdTileCols; kernel 1
+// writes one partial (24 logits and a sum of squares) per tile and token into
+// the workspace, kernel 2 adds them in tile order.
+constexpr int kFwdTileCols = 1024;
+inline int forward_tile_count(int64_t K) {
+    return static_cast<int>((K + kFwdTileCols - 1) / kFwdTileCols);
+}
+// Workspace of the forward: per tile and 16-token step, 8 blocks of 64 FP32
+// (two tokens of 32 floats each: 24 logits, the squares, padding).
+inline uint64_t forward_workspace_bytes(int64_t T, int64_t K) {
+    return static_cast<uint64_t>(forward_tile_count(K)) * static_cast<uint64_t>((T + 15) / 16) *
+           8 * 64 * 4;
+}
+// Units of work of forward kernel 1: tiles x ceil(T / 16); must stay below
+// 2^31.
+inline int64_t forward_units(int64_t T, int64_t K) {
+    return static_cast<int64_t>(forward_tile_count(K)) * ((T + 15) / 16);
+}
 
-// Forward, kernel 0: W [24, K] FP32 -> its TF32 split (BF16 high and low
-// parts of 24 x forward_padded_cols(K) values, zero past K) in wsplit, in the
-// order the pass over X loads it.
-hipError_t launch_split_weight(const Plan &p, const float *w, uint16_t *wsplit, hipStream_t stream,
-                               hipEvent_t start, hipEvent_t stop);
-// Forward, kernel 1: proj [T, 32] (logits in columns 0..23, zeros in 24..31)
-// and r [T] from X and the split W, in one pass over X.
-hipError_t launch_forward(const Plan &p, const float *x, const uint16_t *wsplit, float *proj,
-                          float *r, float eps, hipStream_t stream, hipEvent_t start,
-                          hipEvent_t stop);
+// Forward: kernel 1 (per tile partials into ws) and kernel 2 (proj [T, 32]
+// with the logits in columns 0..23 and zeros in 24..31, r [T]).  The optional
+// events take the start and end times of kernel 1 and the end time of
+// kernel 2.
+hipError_t launch_forward(const Plan &p, const float *x, const float *w, float *proj, float *r,
+                          float eps, float *ws, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t mid, hipEvent_t stop);
 
 }  // namespace mhcpb
 

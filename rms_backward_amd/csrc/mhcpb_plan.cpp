@@ -102,52 +102,36 @@ mhcpb_status_t run(mhcpb_plan_t plan, mhcpb::Outputs out, const float *x, const 
     return MHCPB_SUCCESS;
 }
 
-// Bytes of the forward workspace: the two BF16 planes of the split W, rows
-// padded to whole 64-column chunks.
-uint64_t forward_ws_bytes(const mhcpb::Plan &p) {
-    return 2ull * mhcpb::kProjCols * static_cast<uint64_t>(mhcpb::forward_padded_cols(p.K)) * 2;
-}
-
-// The forward in up to two parts: the weight split (when w is given) into
-// wsplit, then the pass over X (when x is given).  Validates every operand
-// of the parts requested before anything is enqueued.
-mhcpb_status_t run_forward(mhcpb_plan_t plan, bool split, bool pass, const float *x,
-                           const float *w, void *wsplit, size_t wsplit_size, float eps,
-                           float *proj, float *r, hipStream_t stream, hipEvent_t ev_split,
-                           hipEvent_t ev0, hipEvent_t ev1) {
+// The forward: validates every operand, then enqueues its two kernels.
+mhcpb_status_t run_forward(mhcpb_plan_t plan, const float *x, const float *w, float eps,
+                           float *proj, float *r, void *ws, size_t ws_size, hipStream_t stream,
+                           hipEvent_t ev0, hipEvent_t ev1, hipEvent_t ev2) {
     if (!plan)
         return MHCPB_ERROR_INVALID_ARGUMENT;
     const mhcpb::Plan &p = plan->plan;
     const uint64_t T = static_cast<uint64_t>(p.T), K = static_cast<uint64_t>(p.K);
-    const uint64_t wsb = forward_ws_bytes(p);
+    const uint64_t wsb = mhcpb::forward_workspace_bytes(p.T, p.K);
     const Operand ops[] = {
-        {x, T * K * 4, pass},
-        {w, 24 * K * 4, split},
-        {proj, T * 32 * 4, pass},
-        {r, T * 4, pass},
-        {wsplit, wsb, true},
+        {x, T * K * 4, true},     {w, 24 * K * 4, true}, {proj, T * 32 * 4, true},
+        {r, T * 4, true},         {ws, wsb, true},
     };
     constexpr int n = static_cast<int>(sizeof(ops) / sizeof(ops[0]));
     for (int i = 0; i < n; ++i)
-        if (ops[i].required && !ops[i].ptr)
+        if (!ops[i].ptr)
             return MHCPB_ERROR_INVALID_ARGUMENT;
     // eps must be a finite, non-negative FP32 value (a NaN eps would make
     // every RMS NaN).
-    if (pass && !(eps >= 0.0f && eps <= 3.4028234663852886e38f))
+    if (!(eps >= 0.0f && eps <= 3.4028234663852886e38f))
         return MHCPB_ERROR_INVALID_ARGUMENT;
-    if (wsplit_size < wsb)
+    if (mhcpb::forward_units(p.T, p.K) >= (int64_t{1} << 31))
+        return MHCPB_ERROR_UNSUPPORTED;
+    if (ws_size < wsb)
         return MHCPB_ERROR_WORKSPACE;
-    // Only the operands of the requested parts take part in the checks.
-    Operand used[n];
-    for (int i = 0; i < n; ++i)
-        used[i] = ops[i].required ? ops[i] : Operand{nullptr, 0, false};
-    const mhcpb_status_t st = validate_ranges(used, n);
+    const mhcpb_status_t st = validate_ranges(ops, n);
     if (st != MHCPB_SUCCESS)
         return st;
-    auto *ws16 = static_cast<uint16_t *>(wsplit);
-    if (split && mhcpb::launch_split_weight(p, w, ws16, stream, ev_split, nullptr) != hipSuccess)
-        return MHCPB_ERROR_LAUNCH;
-    if (pass && mhcpb::launch_forward(p, x, ws16, proj, r, eps, stream, ev0, ev1) != hipSuccess)
+    if (mhcpb::launch_forward(p, x, w, proj, r, eps, static_cast<float *>(ws), stream, ev0, ev1,
+                              ev2) != hipSuccess)
         return MHCPB_ERROR_LAUNCH;
     return MHCPB_SUCCESS;
 }
@@ -236,37 +220,24 @@ mhcpb_status_t mhcpb_execute_dw(mhcpb_plan_t plan, const float *x, const float *
 mhcpb_status_t mhcpb_forward_workspace_bytes(mhcpb_plan_t plan, size_t *bytes) {
     if (!plan || !bytes)
         return MHCPB_ERROR_INVALID_ARGUMENT;
-    *bytes = static_cast<size_t>(forward_ws_bytes(plan->plan));
+    *bytes = static_cast<size_t>(mhcpb::forward_workspace_bytes(plan->plan.T, plan->plan.K));
     return MHCPB_SUCCESS;
 }
 
 mhcpb_status_t mhcpb_forward(mhcpb_plan_t plan, const float *x, const float *w, float eps,
                              float *proj, float *r, void *workspace, size_t workspace_size,
                              hipStream_t stream) {
-    return run_forward(plan, true, true, x, w, workspace, workspace_size, eps, proj, r, stream,
-                       nullptr, nullptr, nullptr);
+    return run_forward(plan, x, w, eps, proj, r, workspace, workspace_size, stream, nullptr,
+                       nullptr, nullptr);
 }
 
 mhcpb_status_t mhcpb_forward_with_events(mhcpb_plan_t plan, const float *x, const float *w,
                                          float eps, float *proj, float *r, void *workspace,
                                          size_t workspace_size, hipStream_t stream,
-                                         hipEvent_t before_split, hipEvent_t before_pass,
-                                         hipEvent_t after_pass) {
-    return run_forward(plan, true, true, x, w, workspace, workspace_size, eps, proj, r, stream,
-                       before_split, before_pass, after_pass);
-}
-
-mhcpb_status_t mhcpb_forward_prepare_weight(mhcpb_plan_t plan, const float *w, void *wsplit,
-                                            size_t wsplit_size, hipStream_t stream) {
-    return run_forward(plan, true, false, nullptr, w, wsplit, wsplit_size, 0.0f, nullptr, nullptr,
-                       stream, nullptr, nullptr, nullptr);
-}
-
-mhcpb_status_t mhcpb_forward_prepared(mhcpb_plan_t plan, const float *x, const void *wsplit,
-                                      size_t wsplit_size, float eps, float *proj, float *r,
-                                      hipStream_t stream) {
-    return run_forward(plan, false, true, x, nullptr, const_cast<void *>(wsplit), wsplit_size,
-                       eps, proj, r, stream, nullptr, nullptr, nullptr);
+                                         hipEvent_t before_k1, hipEvent_t after_k1,
+                                         hipEvent_t after_k2) {
+    return run_forward(plan, x, w, eps, proj, r, workspace, workspace_size, stream, before_k1,
+                       after_k1, after_k2);
 }
 
 const char *mhcpb_status_string(mhcpb_status_t status) {

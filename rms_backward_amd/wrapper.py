@@ -10,9 +10,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (mhcpb_execute, mhcpb_forward, mhcpb_forward_prepare_weight,
-               mhcpb_forward_prepared, mhcpb_forward_workspace_bytes, mhcpb_plan_create,
-               mhcpb_plan_destroy, mhcpb_workspace_bytes)
+from . import (mhcpb_execute, mhcpb_forward, mhcpb_forward_workspace_bytes,
+               mhcpb_plan_create, mhcpb_plan_destroy, mhcpb_workspace_bytes)
 
 PROJ_COLS = 24
 
@@ -49,16 +48,6 @@ class Plan:
         return mhcpb_forward(self.handle, x, w, eps, proj, r, workspace, workspace.numel(),
                              s.cuda_stream)
 
-    def prepare_weight(self, w, wsplit, stream=None):
-        s = stream if stream is not None else torch.cuda.current_stream(w.device)
-        return mhcpb_forward_prepare_weight(self.handle, w, wsplit, wsplit.numel(),
-                                            s.cuda_stream)
-
-    def forward_prepared(self, x, wsplit, eps, proj, r, stream=None):
-        s = stream if stream is not None else torch.cuda.current_stream(x.device)
-        return mhcpb_forward_prepared(self.handle, x, wsplit, wsplit.numel(), eps, proj, r,
-                                      s.cuda_stream)
-
     def execute(self, x, w, grad_proj, grad_r, r, dx, dw, workspace,
                 grad_x_addend=None, stream=None):
         s = stream if stream is not None else torch.cuda.current_stream(x.device)
@@ -85,7 +74,7 @@ def mhc_projection_forward(x, w, eps: float = 1e-6, stream=None):
     """Allocate outputs and workspace, run the forward map, return (proj, r).
 
     proj is FP32 [T, 32] (logits in columns 0..23, zeros in 24..31), r is
-    FP32 [T].
+    FP32 [T]; the workspace holds the per-tile partials.
     """
     T, K = x.shape
     assert K % 4 == 0

@@ -92,9 +92,9 @@ def sample_cols(K, rng, extra=24, tile=256, whole_first=0):
     return [v for pair in zip(rest, head) for v in pair] + rest[len(head):] + head[len(rest):]
 
 
-def run_forward(x, w, eps=1e-6, plan=None, prepared=False, sync=True):
-    """Forward map once on the current stream over NaN-filled outputs;
-    returns (proj [T, 32], r [T], plan)."""
+def run_forward(x, w, eps=1e-6, plan=None, sync=True):
+    """Forward map once on the current stream over NaN-filled outputs and a
+    NaN-filled workspace; returns (proj [T, 32], r [T], plan)."""
     T, K = x.shape
     if plan is None:
         plan = Plan(T, 4, K // 4)
@@ -102,11 +102,7 @@ def run_forward(x, w, eps=1e-6, plan=None, prepared=False, sync=True):
     r = torch.full((T,), float("nan"), dtype=torch.float32, device=x.device)
     ws = plan.alloc_forward_workspace(x.device)
     ws.fill_(0xFF)
-    if prepared:
-        plan.prepare_weight(w, ws)
-        plan.forward_prepared(x, ws, eps, proj, r)
-    else:
-        plan.forward(x, w, eps, proj, r, ws)
+    plan.forward(x, w, eps, proj, r, ws)
     if sync:
         torch.cuda.synchronize()
     return proj, r, plan

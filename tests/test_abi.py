@@ -229,12 +229,13 @@ def test_split_forms_validate_their_own_operands():
         m.mhcpb_plan_destroy(plan)
 
 
-def test_forward_workspace_is_the_two_weight_planes():
-    for T, hidden in ((1, 2), (4096, 5120), (65536, 512)):
+def test_forward_workspace_is_the_tile_partials():
+    for T, hidden in ((1, 2), (4096, 5120), (65536, 512), (17, 300)):
         plan = m.mhcpb_plan_create(T, 4, hidden)
         try:
-            kp = (4 * hidden + 63) // 64 * 64   # rows padded to whole 64-column chunks
-            assert m.mhcpb_forward_workspace_bytes(plan) == 2 * 24 * kp * 2
+            tiles = (4 * hidden + 1023) // 1024   # partials per 1024-column tile
+            steps = (T + 15) // 16                # 16-token steps: 8 blocks of 64 FP32
+            assert m.mhcpb_forward_workspace_bytes(plan) == tiles * steps * 8 * 64 * 4
         finally:
             m.mhcpb_plan_destroy(plan)
 
@@ -283,23 +284,11 @@ def test_forward_validates_before_any_launch():
         for a, b in (("x", "proj"), ("proj", "r"), ("ws", "w"), ("x", "ws"), ("r", "x")):
             over = {b: fb.addr[a] + fb.size[a] - 16}
             assert _fwd(plan, fb.args(**over), ws) == m.MHCPB_ERROR_OVERLAP, (a, b)
-        # the two halves check only their own operands
-        st = m.mhcpb_forward_prepare_weight(plan, fb.addr["w"], fb.addr["ws"] + 4, ws, 0,
-                                            check=False)
-        assert st == m.MHCPB_ERROR_MISALIGNED
-        st = m.mhcpb_forward_prepare_weight(plan, fb.addr["w"], fb.addr["w"] + 16, ws, 0,
-                                            check=False)
-        assert st == m.MHCPB_ERROR_OVERLAP
-        st = m.mhcpb_forward_prepare_weight(plan, None, fb.addr["ws"], ws, 0, check=False)
-        assert st == m.MHCPB_ERROR_INVALID_ARGUMENT
-        st = m.mhcpb_forward_prepared(plan, fb.addr["x"], fb.addr["ws"], ws, float("nan"),
-                                      fb.addr["proj"], fb.addr["r"], 0, check=False)
-        assert st == m.MHCPB_ERROR_INVALID_ARGUMENT
-        st = m.mhcpb_forward_prepared(plan, fb.addr["x"], fb.addr["ws"], ws - 2, 1e-6,
-                                      fb.addr["proj"], fb.addr["r"], 0, check=False)
-        assert st == m.MHCPB_ERROR_WORKSPACE
-        st = m.mhcpb_forward_prepared(plan, fb.addr["x"], fb.addr["ws"], ws, 1e-6,
-                                      fb.addr["x"] + 64, fb.addr["r"], 0, check=False)
-        assert st == m.MHCPB_ERROR_OVERLAP
+        # too many units of work (tiles x 16-token steps >= 2^31)
+        big = m.mhcpb_plan_create(2**31 - 1, 4, 2**20)
+        try:
+            assert _fwd(big, fb.args(), 1 << 62) == m.MHCPB_ERROR_UNSUPPORTED
+        finally:
+            m.mhcpb_plan_destroy(big)
     finally:
         m.mhcpb_plan_destroy(plan)

@@ -14,7 +14,7 @@ Checks, per case:
   product is exact, with random low bits and TF32 ties on both operands;
 * the pages' sizes (4096 and 16384 tokens, K = 20480) on sampled rows;
 * every row's bits are independent of T and of the other rows, repeat runs
-  and the prepared-weight form give the same bits;
+  and the event-timed form give the same bits;
 * non-finite and extreme rows.
 """
 import math
@@ -130,12 +130,24 @@ def test_rows_do_not_depend_on_t_or_neighbours():
     assert torch.equal(p_perm, p_all[perm]) and torch.equal(r_perm, r_all[perm])
 
 
-def test_prepared_weight_gives_the_same_bits():
+def test_events_form_gives_the_same_bits():
+    import rms_backward_amd as m
+    from bench import HipEvents
     wl = workloads.custom(300, 4, 1030, seed=9)
     inp = workloads.forward_inputs(wl, DEV)
     p1, r1, plan = gh.run_forward(inp["x"], inp["w"])
-    p2, r2, _ = gh.run_forward(inp["x"], inp["w"], plan=plan, prepared=True)
-    assert torch.equal(p1, p2) and torch.equal(r1, r2)
+    proj = torch.full_like(p1, float("nan"))
+    r = torch.full_like(r1, float("nan"))
+    ws = plan.alloc_forward_workspace(DEV)
+    hev = HipEvents()
+    ev = [hev.create() for _ in range(3)]
+    m.mhcpb_forward_with_events(plan.handle, inp["x"], inp["w"], 1e-6, proj, r, ws, ws.numel(),
+                                torch.cuda.current_stream().cuda_stream, *ev)
+    torch.cuda.synchronize()
+    assert hev.elapsed_ms(ev[0], ev[1]) > 0 and hev.elapsed_ms(ev[1], ev[2]) > 0
+    for e in ev:
+        hev.destroy(e)
+    assert torch.equal(p1, proj) and torch.equal(r1, r)
 
 
 def test_non_finite_and_extreme_rows():
