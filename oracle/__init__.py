@@ -63,6 +63,9 @@ def _load():
         lib.oracle_forward.argtypes = [ctypes.c_int, i64, i64, f32p, f32p,
                                        ctypes.c_double, f64p, f64p]
         lib.oracle_forward.restype = ctypes.c_int
+        lib.oracle_rmsnorm_backward.argtypes = [i64, i64, u16p, u16p, f32p, f32p, u16p, f64p,
+                                                f64p]
+        lib.oracle_rmsnorm_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -165,3 +168,32 @@ def forward(x, w, eps: float = 1e-6, mode: str = "tf32"):
     if rc != 0:
         raise ValueError("oracle_forward rejected its arguments")
     return proj, r
+
+
+def rmsnorm_backward(g_bits, x_bits, w, rstd, res_bits=None):
+    """(dx [rows, H], dw [H]) in FP64 for the BF16 RMSNorm backward: g, x and
+    res as BF16 bit patterns (uint16), w the weight's values (FP32 array;
+    BF16 weights widened), rstd [rows] FP32 from the forward."""
+    lib = _load()
+    g_bits = np.ascontiguousarray(g_bits, dtype=np.uint16)
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, H = x_bits.shape
+    assert g_bits.shape == (rows, H)
+    w, wp = _f32(w)
+    rs, rsp = _f32(rstd)
+    assert w.shape == (H,) and rs.shape == (rows,)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    rp = None
+    if res_bits is not None:
+        res_bits = np.ascontiguousarray(res_bits, dtype=np.uint16)
+        assert res_bits.shape == (rows, H)
+        rp = res_bits.ctypes.data_as(u16p)
+    dx = np.empty((rows, H), dtype=np.float64)
+    dw = np.empty((H,), dtype=np.float64)
+    rc = lib.oracle_rmsnorm_backward(rows, H, g_bits.ctypes.data_as(u16p),
+                                     x_bits.ctypes.data_as(u16p), wp, rsp, rp,
+                                     dx.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                     dw.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError("oracle_rmsnorm_backward rejected its arguments")
+    return dx, dw

@@ -28,6 +28,8 @@
  * X W^T (TF32 operands in mode 1) and the row RMS sqrt(mean(x^2) + eps) in
  * FP32-range arithmetic on the raw x (see its own comment).
  *
+ * oracle_rmsnorm_backward is a second workload (see its own comment).
+ *
  * Rounding here is done arithmetically (frexp / ldexp / nearbyint under
  * round-to-nearest-even), deliberately not by bit manipulation.
  *
@@ -234,6 +236,54 @@ int oracle_forward(int mode, int64_t rows, int64_t K, const float *x,
         if (ss > (double)FLT_MAX)
             ss = INFINITY;
         r[t] = sqrt(ss / (double)K + eps);
+    }
+    return 0;
+}
+
+/*
+ * A second workload: the backward of a BF16 RMSNorm, y = x * rstd * w per
+ * row, rstd = 1 / sqrt(mean(x^2) + eps) given by the forward
+ * ("flashinfer.cake_rmsnorm_det_train.cake_rmsnorm_det_train_backward" page,
+ * its signature and parameter list: BF16 g and x, BF16 or FP32 w, FP32 rstd,
+ * optional BF16 g_residual added once, BF16 dx and FP32 dw).  The page does
+ * not print the formula; this is the textbook gradient of that map with rstd
+ * taken as the forward gave it:
+ *
+ *   c1[t]   = sum_h w[h] g[t,h] x[t,h] / H
+ *   dx[t,h] = rstd[t] w[h] g[t,h] - rstd[t]^3 c1[t] x[t,h]  [+ g_residual]
+ *   dw[h]   = sum_t g[t,h] x[t,h] rstd[t]
+ *
+ * (rstd depends on x: d rstd / d x[t,h] = -rstd^3 x[t,h] / H.)  Evaluated in
+ * FP64 from the exact input values, no final rounding.
+ *
+ *   g, x, res  [rows, H] BF16 bits (res may be NULL)
+ *   w          [H] the weight's values (BF16 or FP32, widened exactly)
+ *   rstd       [rows]
+ *   dx         [rows, H] FP64 out;  dw [H] FP64 out (summed over the rows)
+ */
+int oracle_rmsnorm_backward(int64_t rows, int64_t H, const uint16_t *g, const uint16_t *x,
+                            const float *w, const float *rstd, const uint16_t *res,
+                            double *dx, double *dw)
+{
+    if (rows < 0 || H <= 0)
+        return -1;
+    for (int64_t h = 0; h < H; ++h)
+        dw[h] = 0.0;
+    for (int64_t t = 0; t < rows; ++t) {
+        const uint16_t *gt = g + t * H, *xt = x + t * H;
+        double c1 = 0.0;
+        for (int64_t h = 0; h < H; ++h)
+            c1 += (double)w[h] * bf16_bits_to_double(gt[h]) * bf16_bits_to_double(xt[h]);
+        c1 /= (double)H;
+        const double rs = (double)rstd[t];
+        for (int64_t h = 0; h < H; ++h) {
+            const double gv = bf16_bits_to_double(gt[h]), xv = bf16_bits_to_double(xt[h]);
+            double v = rs * (double)w[h] * gv - rs * rs * rs * c1 * xv;
+            if (res)
+                v += bf16_bits_to_double(res[t * H + h]);
+            dx[t * H + h] = v;
+            dw[h] += gv * xv * rs;
+        }
     }
     return 0;
 }
