@@ -1,7 +1,7 @@
 """Benchmark of the DSv4.1 mHC projection/RMS backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
-                    [--stage backward|forward] [--form fused|split]
+                    [--stage backward|forward|rmsnorm] [--form fused|split]
 
 One step is one call of mhcpb_execute (kernel 1 + kernel 2) on the synthetic
 workload, with every input already resident in HBM.  Prints ONE JSON line:
@@ -363,6 +363,180 @@ def run_forward(args, wl) -> dict:
     }
 
 
+RMS_METRIC = ("BF16 RMSNorm backward: µs/call and achieved HBM GB/s (% of peak) at "
+              "T=4096, H=5120")
+RMS_SOURCES = [os.path.join(ROOT, "rms_backward_amd", "csrc", n)
+               for n in ("mhcpb_rmsnorm.hip", "mhcpb_device.h")]
+RMS_COUNTERS_FILE = os.path.join(ROOT, "profiles", "rmsnorm_train_counters.json")
+
+
+def rms_schedule(T: int, H: int) -> int:
+    """Blocks S of the RMSNorm backward (a function of T and H only)."""
+    if T == 0:
+        return 0
+    nc = -(-H // 512)
+    return min(-(-T // 16), 256 * max(1, 12 // nc))
+
+
+def rms_bytes(T: int, H: int, w_f32: bool, residual: bool) -> tuple[int, int, int]:
+    """(whole call, kernel 1, partial-free) algorithmic bytes of the RMSNorm
+    backward: g, x (and g_residual) read and dx written once (BF16), w and
+    rstd read, dw written, and the S block partials of dw written by kernel 1
+    and read by kernel 2."""
+    S = rms_schedule(T, H)
+    rows = T * H * 2 * (3 + (1 if residual else 0))
+    small = H * (4 if w_f32 else 2) + T * 4
+    partials = S * H * 4
+    io = rows + small + H * 4
+    return io + 2 * partials, rows + small + partials, io
+
+
+def rms_source_hash() -> str:
+    text = ""
+    for path in RMS_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            text += f.read() + "\n"
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()[:16]
+
+
+def rms_traffic(workload: str):
+    """HBM bytes per rows-kernel launch from the committed counter summary, if
+    taken on the current source; otherwise None."""
+    try:
+        with open(RMS_COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != rms_source_hash():
+        return None
+    if rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def rms_cpu_baseline(inp, wl, min_seconds: float = 2.0):
+    """Time the FP64 oracle (as it is, one thread) on the whole workload,
+    repeated until at least `min_seconds` have passed."""
+    import oracle
+    from tests import gpu_harness as gh
+    g = gh.bf16_bits_np(inp["g"])
+    x = gh.bf16_bits_np(inp["x"])
+    w = inp["w"].float().cpu().numpy()
+    rstd = inp["rstd"].cpu().numpy()
+    res = gh.bf16_bits_np(inp["res"]) if inp.get("res") is not None else None
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.rmsnorm_backward(g, x, w, rstd, res_bits=res)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    call_bytes, _, _ = rms_bytes(wl.T, wl.H, wl.w_f32, wl.residual)
+    return {
+        "value": round(call_bytes * reps / dt / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"the whole workload (all {wl.T} rows, dx and dw), FP64 oracle, one "
+                   f"thread, {reps} call(s) in {dt:.2f} s"),
+        "us_per_call_extrapolated": round(dt / reps * 1e6, 1),
+    }
+
+
+def run_rmsnorm(args, wl) -> dict:
+    """The second workload: per step one mhcpb_rmsnorm_backward call (the rows
+    kernel, then the fixed-order sum of the block partials)."""
+    import torch
+    import workloads
+    import rms_backward_amd as m
+
+    T, H = wl.T, wl.H
+    inp = workloads.rms_inputs(wl, "cuda")
+    dx = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dw = torch.full((H,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, m.mhcpb_rmsnorm_backward_workspace_bytes(T, H)), dtype=torch.uint8,
+                     device="cuda")
+    wd = m.MHCPB_DTYPE_F32 if wl.w_f32 else m.MHCPB_DTYPE_BF16
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    call = lambda: m.mhcpb_rmsnorm_backward(T, H, inp["g"], inp["x"], inp["w"], wd, inp["rstd"],
+                                            inp["res"], dx, dw, ws, ws.numel(), sh)
+    for _ in range(args.warmup):
+        call()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us_per_call = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    hev = HipEvents()
+    n = args.steps
+    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b, c in evs:
+        m.mhcpb_rmsnorm_backward_with_events(T, H, inp["g"], inp["x"], inp["w"], wd, inp["rstd"],
+                                             inp["res"], dx, dw, ws, ws.numel(), sh, a, b, c)
+    torch.cuda.synchronize()
+    k1_ms = [hev.elapsed_ms(a, b) for a, b, _ in evs]
+    k2_ms = [hev.elapsed_ms(b, c) for _, b, c in evs]
+    for trio in evs:
+        for e in trio:
+            hev.destroy(e)
+    k1_us = sum(k1_ms) / n * 1e3
+    k2_us = sum(k2_ms) / n * 1e3
+    S = rms_schedule(T, H)
+    call_bytes, k1_bytes, io_bytes = rms_bytes(T, H, wl.w_f32, wl.residual)
+    gbps = call_bytes / (us_per_call * 1e-6) / 1e9
+    k1_gbps = k1_bytes / (k1_us * 1e-6) / 1e9
+    return {
+        "metric": RMS_METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_call / 1e3, 6),
+        "us_per_call": round(us_per_call, 2),
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name} RMSNorm backward: T={T} rows, H={H}; g, x BF16, w "
+                         f"{'FP32' if wl.w_f32 else 'BF16'}, rstd FP32"
+                         + (", g_residual BF16" if wl.residual else "")
+                         + "; dx BF16, dw FP32"),
+            "stage": "rmsnorm", "T": T, "H": H, "blocks": S,
+            "bytes_per_call": call_bytes,
+            "bytes_per_call_without_partials": io_bytes,
+            "k1_us": round(k1_us, 2), "k2_us": round(k2_us, 2),
+            "timed_wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(k1_gbps, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": rms_traffic(wl.name),
+            "kernel": "RMSNorm backward rows (rmsnorm_bwd_rows, kernel 1)",
+            "bytes_per_launch": k1_bytes,
+        },
+        "_inputs": inp,
+    }
+
+
 def run_copy_calibration(nbytes: int, reps: int):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -386,9 +560,10 @@ def main(argv=None):
     ap.add_argument("--form", choices=("fused", "split"), default="fused",
                     help="fused: mhcpb_execute per step; split: mhcpb_execute_dx then "
                          "mhcpb_execute_dw per step (X read twice)")
-    ap.add_argument("--stage", choices=("backward", "forward"), default="backward",
+    ap.add_argument("--stage", choices=("backward", "forward", "rmsnorm"), default="backward",
                     help="backward: the stage (default); forward: the map it differentiates "
-                         "(mhcpb_forward: proj = X W^T and r per step)")
+                         "(mhcpb_forward: proj = X W^T and r per step); rmsnorm: the BF16 "
+                         "RMSNorm backward (workloads rms_*, default rms_train)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter scaling)")
     args = ap.parse_args(argv)
@@ -409,6 +584,21 @@ def main(argv=None):
     from rms_backward_amd import mhcpb_execute_with_events, mhcpb_plan_split_count
     from rms_backward_amd.wrapper import Plan
     from tests import gpu_harness as gh
+
+    if args.stage == "rmsnorm":
+        name = "rms_train" if args.workload == "train" else args.workload
+        wl = workloads.RMS_WORKLOADS[name]
+        print(f"bench: workload {wl.name} T={wl.T} H={wl.H} stage rmsnorm", file=sys.stderr,
+              flush=True)
+        out = run_rmsnorm(args, wl)
+        inp = out.pop("_inputs")
+        if not args.no_cpu_baseline:
+            print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+            out["cpu_baseline"] = rms_cpu_baseline(inp, wl)
+        else:
+            out["cpu_baseline"] = None
+        print(json.dumps(out), flush=True)
+        return 0
 
     wl = workloads.WORKLOADS[args.workload]
     T, K = wl.T, wl.K

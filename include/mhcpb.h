@@ -209,6 +209,84 @@ mhcpb_status_t mhcpb_forward_with_events(mhcpb_plan_t plan, const float *x, cons
                                          hipEvent_t before_k1, hipEvent_t after_k1,
                                          hipEvent_t after_k2);
 
+/*
+ * A second workload: the deterministic BF16 RMSNorm backward of the
+ * "flashinfer.cake_rmsnorm_det_train.cake_rmsnorm_det_train_backward" page
+ * (its signature, parameters and the notes on program selection).  For
+ * y = x * rstd * w per row of x [T, H],
+ *
+ *     c1[t]   = sum_h w[h] g[t, h] x[t, h] / H
+ *     dx[t, h] = rstd[t] w[h] g[t, h] - rstd[t]^3 c1[t] x[t, h]
+ *                (+ g_residual[t, h])                      BF16, one rounding
+ *     dw[h]   = sum_t g[t, h] x[t, h] rstd[t]               FP32
+ *
+ * (the page prints no formula: this is the gradient of that map with rstd
+ * taken as the forward returned it).  dx is computed in FP32 and rounded to
+ * BF16 once, the residual gradient added a single time, before that rounding.
+ * dw is reduced from per-block partials in a fixed order: the rows are dealt
+ * round-robin to S = min(ceil(T / 16), 256 * max(1, 12 / ceil(H / 512)))
+ * blocks, a function of (T, H) alone, so dw is bitwise reproducible for a
+ * given (T, H) on any device, whatever its CU count; each row's dx depends
+ * on that row alone.
+ *
+ * Workspace: S * H * 4 bytes (one FP32 partial dw per block; 0 when T = 0).
+ */
+typedef enum mhcpb_dtype {
+    MHCPB_DTYPE_BF16 = 0,
+    MHCPB_DTYPE_F32 = 1
+} mhcpb_dtype_t;
+
+/*
+ * Bytes of workspace mhcpb_rmsnorm_backward needs for T rows of width H.
+ * MHCPB_ERROR_INVALID_ARGUMENT for T < 0, H < 1 or a NULL `bytes`;
+ * MHCPB_ERROR_UNSUPPORTED for a shape mhcpb_rmsnorm_backward rejects as such.
+ */
+mhcpb_status_t mhcpb_rmsnorm_backward_workspace_bytes(int64_t T, int32_t H, size_t *bytes);
+
+/*
+ * Enqueue the RMSNorm backward on `stream`: kernel 1 reads g, x (and
+ * g_residual) once, writes dx and one partial dw per block; kernel 2 adds the
+ * partials in a fixed order into dw.  With T = 0 only kernel 2 runs and dw
+ * becomes +0.
+ *
+ *   T, H        rows and width; 0 <= T <= 2^31 - 1; H a multiple of 8 (rows of
+ *               16-byte multiples, as the page requires for in-place reads)
+ *               with 8 <= H <= 6144 (the page's widths go up to 6144), else
+ *               MHCPB_ERROR_UNSUPPORTED
+ *   g, x        [T, H] BF16 bit patterns, row-major and compact
+ *   w           [H] BF16 (w_dtype MHCPB_DTYPE_BF16) or FP32 (MHCPB_DTYPE_F32)
+ *   rstd        [T] FP32 reciprocal RMS of the forward (any value; IEEE
+ *               arithmetic follows)
+ *   g_residual  [T, H] BF16 or NULL
+ *   dx          [T, H] BF16 out, overwritten
+ *   dw          [H] FP32 out, overwritten
+ *   workspace   >= mhcpb_rmsnorm_backward_workspace_bytes(T, H) bytes of
+ *               device memory (may be NULL when that is 0); contents
+ *               undefined on entry and exit
+ *
+ * Pointers that take part must be 16-byte aligned and their byte ranges
+ * disjoint (MHCPB_ERROR_MISALIGNED, MHCPB_ERROR_OVERLAP); g, x, rstd and dx
+ * may be NULL only when T = 0; w and dw are always required.  Like
+ * mhcpb_execute it only validates and launches, allocates nothing, and on any
+ * error launches nothing.
+ */
+mhcpb_status_t mhcpb_rmsnorm_backward(int64_t T, int32_t H, const uint16_t *g, const uint16_t *x,
+                                      const void *w, mhcpb_dtype_t w_dtype, const float *rstd,
+                                      const uint16_t *g_residual, uint16_t *dx, float *dw,
+                                      void *workspace, size_t workspace_size, hipStream_t stream);
+
+/*
+ * mhcpb_rmsnorm_backward with caller-owned events: `before_k1` and `after_k1`
+ * take the start and end times of kernel 1, `after_k2` the end time of
+ * kernel 2 (when T = 0 the first two are recorded just before kernel 2).
+ * Any may be NULL.
+ */
+mhcpb_status_t mhcpb_rmsnorm_backward_with_events(
+    int64_t T, int32_t H, const uint16_t *g, const uint16_t *x, const void *w,
+    mhcpb_dtype_t w_dtype, const float *rstd, const uint16_t *g_residual, uint16_t *dx,
+    float *dw, void *workspace, size_t workspace_size, hipStream_t stream,
+    hipEvent_t before_k1, hipEvent_t after_k1, hipEvent_t after_k2);
+
 /* A static, human-readable name for a status code. */
 const char *mhcpb_status_string(mhcpb_status_t status);
 

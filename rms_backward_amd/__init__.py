@@ -41,7 +41,12 @@ EXPORTED = (
     "mhcpb_plan_split_count", "mhcpb_execute", "mhcpb_execute_with_events",
     "mhcpb_execute_dx", "mhcpb_execute_dw", "mhcpb_status_string",
     "mhcpb_forward_workspace_bytes", "mhcpb_forward", "mhcpb_forward_with_events",
+    "mhcpb_rmsnorm_backward_workspace_bytes", "mhcpb_rmsnorm_backward",
+    "mhcpb_rmsnorm_backward_with_events",
 )
+
+MHCPB_DTYPE_BF16 = 0
+MHCPB_DTYPE_F32 = 1
 
 _vp = ctypes.c_void_p
 _lib.mhcpb_plan_create.argtypes = [ctypes.POINTER(_vp), ctypes.c_int64, ctypes.c_int32,
@@ -69,6 +74,15 @@ _lib.mhcpb_forward.argtypes = _FWD_ARGS
 _lib.mhcpb_forward.restype = ctypes.c_int
 _lib.mhcpb_forward_with_events.argtypes = _FWD_ARGS + [_vp, _vp, _vp]
 _lib.mhcpb_forward_with_events.restype = ctypes.c_int
+_lib.mhcpb_rmsnorm_backward_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+_lib.mhcpb_rmsnorm_backward_workspace_bytes.restype = ctypes.c_int
+_RMS_ARGS = [ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+             _vp, ctypes.c_size_t, _vp]
+_lib.mhcpb_rmsnorm_backward.argtypes = _RMS_ARGS
+_lib.mhcpb_rmsnorm_backward.restype = ctypes.c_int
+_lib.mhcpb_rmsnorm_backward_with_events.argtypes = _RMS_ARGS + [_vp, _vp, _vp]
+_lib.mhcpb_rmsnorm_backward_with_events.restype = ctypes.c_int
 _lib.mhcpb_status_string.argtypes = [ctypes.c_int]
 _lib.mhcpb_status_string.restype = ctypes.c_char_p
 
@@ -204,4 +218,44 @@ def mhcpb_forward_with_events(plan, x, w, eps: float, proj, r, workspace, worksp
                                         before_k1, after_k1, after_k2)
     if check and st != MHCPB_SUCCESS:
         raise MhcpbError(st, "mhcpb_forward_with_events")
+    return st
+
+
+def mhcpb_rmsnorm_backward_workspace_bytes(T: int, H: int, check: bool = True):
+    """Workspace bytes of the RMSNorm backward for T rows of width H; with
+    ``check`` False returns (status, bytes) instead of raising."""
+    n = ctypes.c_size_t()
+    st = _lib.mhcpb_rmsnorm_backward_workspace_bytes(int(T), int(H), ctypes.byref(n))
+    if not check:
+        return st, n.value
+    if st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_rmsnorm_backward_workspace_bytes")
+    return n.value
+
+
+def mhcpb_rmsnorm_backward(T: int, H: int, g, x, w, w_dtype: int, rstd, g_residual, dx, dw,
+                           workspace, workspace_size: int, stream: int = 0,
+                           check: bool = True) -> int:
+    """Enqueue the BF16 RMSNorm backward (dx BF16, dw FP32).  BF16 tensors are
+    passed by device address (torch bfloat16 or int16 tensors, or ints)."""
+    st = _lib.mhcpb_rmsnorm_backward(int(T), int(H), _ptr(g), _ptr(x), _ptr(w), int(w_dtype),
+                                     _ptr(rstd), _ptr(g_residual), _ptr(dx), _ptr(dw),
+                                     _ptr(workspace), int(workspace_size), stream)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_rmsnorm_backward")
+    return st
+
+
+def mhcpb_rmsnorm_backward_with_events(T: int, H: int, g, x, w, w_dtype: int, rstd, g_residual,
+                                       dx, dw, workspace, workspace_size: int, stream: int,
+                                       before_k1: int | None, after_k1: int | None,
+                                       after_k2: int | None, check: bool = True) -> int:
+    """mhcpb_rmsnorm_backward with caller-owned hipEvent_t handles on the
+    dispatches (start and end of kernel 1, end of kernel 2)."""
+    st = _lib.mhcpb_rmsnorm_backward_with_events(
+        int(T), int(H), _ptr(g), _ptr(x), _ptr(w), int(w_dtype), _ptr(rstd), _ptr(g_residual),
+        _ptr(dx), _ptr(dw), _ptr(workspace), int(workspace_size), stream, before_k1, after_k1,
+        after_k2)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_rmsnorm_backward_with_events")
     return st

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmhcpb.so")
 
-SOURCES = ["mhcpb_plan.cpp", "mhcpb_kernels.hip", "mhcpb_forward.hip"]
+SOURCES = ["mhcpb_plan.cpp", "mhcpb_kernels.hip", "mhcpb_forward.hip", "mhcpb_rmsnorm.hip"]
 
 # Packed FP32 VALU instructions stay disabled: they are not used anywhere.
 HIPCC_FLAGS = [

@@ -82,6 +82,57 @@ hipError_t launch_forward(const Plan &p, const float *x, const float *w, float *
                           float eps, float *ws, hipStream_t stream, hipEvent_t start,
                           hipEvent_t mid, hipEvent_t stop);
 
+// BF16 RMSNorm backward (second workload).  A row is cut into chunks of
+// 512 columns, one wave each; a block has one wave per chunk.  Rows are
+// dealt to S blocks round-robin (block b takes rows b, b + S, ...), with
+// S = min(ceil(T / 16), 256 * P) and P = max(1, 12 / chunks) blocks per CU's
+// worth of waves: a function of (T, H) only, never of the device.  The
+// workspace holds one FP32 partial dw [H] per block.
+#ifndef MHCPB_RMS_MAX_BLOCKS
+#define MHCPB_RMS_MAX_BLOCKS 256
+#endif
+#ifndef MHCPB_RMS_MIN_ROWS
+#define MHCPB_RMS_MIN_ROWS 16
+#endif
+constexpr int64_t kRmsBlockUnit = MHCPB_RMS_MAX_BLOCKS;
+constexpr int64_t kRmsMinRowsPerBlock = MHCPB_RMS_MIN_ROWS;
+constexpr int kRmsChunkCols = 512;
+constexpr int kRmsWavesPerUnit = 12;
+constexpr int32_t kRmsMaxH = 6144;  // 12 chunks of 512 columns
+
+inline int rmsnorm_chunks(int32_t H) { return (H + kRmsChunkCols - 1) / kRmsChunkCols; }
+
+struct RmsPlan {
+    int64_t T;
+    int32_t H;
+    int64_t S;  // blocks (and partials)
+};
+
+inline RmsPlan rmsnorm_plan(int64_t T, int32_t H) {
+    RmsPlan p{T, H, 0};
+    if (T > 0) {
+        const int nc = rmsnorm_chunks(H);
+        const int64_t per_unit = nc >= kRmsWavesPerUnit ? 1 : kRmsWavesPerUnit / nc;
+        int64_t s = (T + kRmsMinRowsPerBlock - 1) / kRmsMinRowsPerBlock;
+        if (s > kRmsBlockUnit * per_unit) s = kRmsBlockUnit * per_unit;
+        p.S = s;
+    }
+    return p;
+}
+
+inline uint64_t rmsnorm_workspace_bytes(const RmsPlan &p) {
+    return static_cast<uint64_t>(p.S) * static_cast<uint64_t>(p.H) * 4;
+}
+
+// Kernel 1 (dx and the block partials; skipped when T = 0) and kernel 2 (dw
+// from the partials).  The optional events take the start and end times of
+// kernel 1 and the end time of kernel 2.
+hipError_t launch_rmsnorm_backward(const RmsPlan &p, const uint16_t *g, const uint16_t *x,
+                                   const void *w, bool w_f32, const float *rstd,
+                                   const uint16_t *res, uint16_t *dx, float *dw, float *ws,
+                                   hipStream_t stream, hipEvent_t start, hipEvent_t mid,
+                                   hipEvent_t stop);
+
 }  // namespace mhcpb
 
 struct mhcpb_plan_s {

@@ -136,6 +136,58 @@ mhcpb_status_t run_forward(mhcpb_plan_t plan, const float *x, const float *w, fl
     return MHCPB_SUCCESS;
 }
 
+// Shape check of the RMSNorm backward: status, and the block schedule.
+mhcpb_status_t rmsnorm_shape(int64_t T, int32_t H, mhcpb::RmsPlan *p) {
+    if (T < 0 || H < 1)
+        return MHCPB_ERROR_INVALID_ARGUMENT;
+    if (T > kMaxT || H > mhcpb::kRmsMaxH || H < 8 || (H % 8) != 0)
+        return MHCPB_ERROR_UNSUPPORTED;
+    *p = mhcpb::rmsnorm_plan(T, H);
+    return MHCPB_SUCCESS;
+}
+
+mhcpb_status_t run_rmsnorm(int64_t T, int32_t H, const uint16_t *g, const uint16_t *x,
+                           const void *w, mhcpb_dtype_t w_dtype, const float *rstd,
+                           const uint16_t *res, uint16_t *dx, float *dw, void *ws,
+                           size_t ws_size, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
+                           hipEvent_t ev2) {
+    mhcpb::RmsPlan p{};
+    const mhcpb_status_t shape = rmsnorm_shape(T, H, &p);
+    if (shape != MHCPB_SUCCESS)
+        return shape;
+    if (w_dtype != MHCPB_DTYPE_BF16 && w_dtype != MHCPB_DTYPE_F32)
+        return MHCPB_ERROR_INVALID_ARGUMENT;
+    const uint64_t rows = static_cast<uint64_t>(T), h = static_cast<uint64_t>(H);
+    const uint64_t wsb = mhcpb::rmsnorm_workspace_bytes(p);
+    const bool any = T > 0;
+    const Operand ops[] = {
+        {g, rows * h * 2, any},
+        {x, rows * h * 2, any},
+        {w, h * (w_dtype == MHCPB_DTYPE_F32 ? 4 : 2), true},
+        {rstd, rows * 4, any},
+        {res, rows * h * 2, false},
+        {dx, rows * h * 2, any},
+        {dw, h * 4, true},
+        {ws, wsb, wsb > 0},
+    };
+    constexpr int n = static_cast<int>(sizeof(ops) / sizeof(ops[0]));
+    for (int i = 0; i < n; ++i)
+        if (ops[i].required && !ops[i].ptr)
+            return MHCPB_ERROR_INVALID_ARGUMENT;
+    if (ws_size < wsb)
+        return MHCPB_ERROR_WORKSPACE;
+    // With no rows only w, dw and the workspace take part.
+    const Operand used[] = {ops[2], ops[6], ops[7]};
+    const mhcpb_status_t st = any ? validate_ranges(ops, n) : validate_ranges(used, 3);
+    if (st != MHCPB_SUCCESS)
+        return st;
+    if (mhcpb::launch_rmsnorm_backward(p, g, x, w, w_dtype == MHCPB_DTYPE_F32, rstd, res, dx, dw,
+                                       static_cast<float *>(ws), stream, ev0, ev1,
+                                       ev2) != hipSuccess)
+        return MHCPB_ERROR_LAUNCH;
+    return MHCPB_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -238,6 +290,35 @@ mhcpb_status_t mhcpb_forward_with_events(mhcpb_plan_t plan, const float *x, cons
                                          hipEvent_t after_k2) {
     return run_forward(plan, x, w, eps, proj, r, workspace, workspace_size, stream, before_k1,
                        after_k1, after_k2);
+}
+
+mhcpb_status_t mhcpb_rmsnorm_backward_workspace_bytes(int64_t T, int32_t H, size_t *bytes) {
+    if (!bytes)
+        return MHCPB_ERROR_INVALID_ARGUMENT;
+    mhcpb::RmsPlan p{};
+    const mhcpb_status_t st = rmsnorm_shape(T, H, &p);
+    if (st != MHCPB_SUCCESS)
+        return st;
+    *bytes = static_cast<size_t>(mhcpb::rmsnorm_workspace_bytes(p));
+    return MHCPB_SUCCESS;
+}
+
+mhcpb_status_t mhcpb_rmsnorm_backward(int64_t T, int32_t H, const uint16_t *g, const uint16_t *x,
+                                      const void *w, mhcpb_dtype_t w_dtype, const float *rstd,
+                                      const uint16_t *g_residual, uint16_t *dx, float *dw,
+                                      void *workspace, size_t workspace_size,
+                                      hipStream_t stream) {
+    return run_rmsnorm(T, H, g, x, w, w_dtype, rstd, g_residual, dx, dw, workspace,
+                       workspace_size, stream, nullptr, nullptr, nullptr);
+}
+
+mhcpb_status_t mhcpb_rmsnorm_backward_with_events(
+    int64_t T, int32_t H, const uint16_t *g, const uint16_t *x, const void *w,
+    mhcpb_dtype_t w_dtype, const float *rstd, const uint16_t *g_residual, uint16_t *dx,
+    float *dw, void *workspace, size_t workspace_size, hipStream_t stream,
+    hipEvent_t before_k1, hipEvent_t after_k1, hipEvent_t after_k2) {
+    return run_rmsnorm(T, H, g, x, w, w_dtype, rstd, g_residual, dx, dw, workspace,
+                       workspace_size, stream, before_k1, after_k1, after_k2);
 }
 
 const char *mhcpb_status_string(mhcpb_status_t status) {

@@ -10,8 +10,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (mhcpb_execute, mhcpb_forward, mhcpb_forward_workspace_bytes,
-               mhcpb_plan_create, mhcpb_plan_destroy, mhcpb_workspace_bytes)
+from . import (MHCPB_DTYPE_BF16, MHCPB_DTYPE_F32, mhcpb_execute, mhcpb_forward,
+               mhcpb_forward_workspace_bytes, mhcpb_plan_create, mhcpb_plan_destroy,
+               mhcpb_rmsnorm_backward, mhcpb_rmsnorm_backward_workspace_bytes,
+               mhcpb_workspace_bytes)
 
 PROJ_COLS = 24
 
@@ -84,3 +86,30 @@ def mhc_projection_forward(x, w, eps: float = 1e-6, stream=None):
     ws = plan.alloc_forward_workspace(x.device)
     plan.forward(x, w, eps, proj, r, ws, stream)
     return proj, r
+
+
+def rmsnorm_backward(g, x, w, rstd, g_residual=None, workspace=None, dx=None, dw=None,
+                     stream=None):
+    """The deterministic BF16 RMSNorm backward: returns (dx, dw), dx BF16 of
+    x's shape [T, H], dw FP32 [H].  g, x (and g_residual) are compact BF16
+    [T, H]; w is BF16 or FP32 [H]; rstd FP32 [T].  Outputs and the workspace
+    are allocated when not given."""
+    T, H = x.shape
+    dev = x.device
+    if w.dtype == torch.float32:
+        wd = MHCPB_DTYPE_F32
+    elif w.dtype == torch.bfloat16:
+        wd = MHCPB_DTYPE_BF16
+    else:
+        raise TypeError(f"w must be bfloat16 or float32, got {w.dtype}")
+    if dx is None:
+        dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    if dw is None:
+        dw = torch.empty(H, dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = mhcpb_rmsnorm_backward_workspace_bytes(T, H)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    mhcpb_rmsnorm_backward(T, H, g, x, w, wd, rstd, g_residual, dx, dw, workspace,
+                           workspace.numel(), s.cuda_stream)
+    return dx, dw

@@ -106,3 +106,32 @@ def run_forward(x, w, eps=1e-6, plan=None, sync=True):
     if sync:
         torch.cuda.synchronize()
     return proj, r, plan
+
+
+def run_rmsnorm(inp, poison=True, sync=True, workspace=None):
+    """RMSNorm backward once on the current stream; returns (dx, dw)."""
+    from rms_backward_amd.wrapper import rmsnorm_backward
+    x = inp["x"]
+    T, H = x.shape
+    dx = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    dw = torch.empty(H, dtype=torch.float32, device=x.device)
+    if poison:
+        dx.fill_(float("nan"))
+        dw.fill_(float("nan"))
+    rmsnorm_backward(inp["g"], x, inp["w"], inp["rstd"], inp.get("res"), workspace=workspace,
+                     dx=dx, dw=dw)
+    if sync:
+        torch.cuda.synchronize()
+    return dx, dw
+
+
+def rms_oracle(inp, rows=None):
+    """Oracle (dx [rows, H], dw [H] over the given rows) from device inputs."""
+    import oracle
+    sel = (lambda t: t) if rows is None else (lambda t: t[rows])
+    g = bf16_bits_np(sel(inp["g"]))
+    x = bf16_bits_np(sel(inp["x"]))
+    w = inp["w"].float().cpu().numpy()
+    rstd = host(sel(inp["rstd"]))
+    res = bf16_bits_np(sel(inp["res"])) if inp.get("res") is not None else None
+    return oracle.rmsnorm_backward(g, x, w, rstd, res_bits=res)

@@ -72,3 +72,63 @@ def fwd_r_rel_bound(K):
     and the square root."""
     u = 2.0 ** -24
     return (K / 4 + 64) * u / 2 + 3 * u
+
+
+# ---- BF16 RMSNorm backward ---------------------------------------------------
+U32 = 2.0 ** -24
+
+
+def rms_dx_fp32_error(g, x, w, rstd, res, H):
+    """Worst-case error of the FP32 value the GPU rounds to BF16, per element.
+
+    c1 = sum_h w g x / H is summed with fused multiply-adds over at most 96
+    terms per lane and a 6-level tree across 64 lanes (<= 103 roundings), then
+    divided by H and multiplied by rstd three times (4 roundings); the value
+    rstd w g - k x takes three roundings and the residual one more."""
+    g, x, w = (np.asarray(a, dtype=np.float64) for a in (g, x, w))
+    rs = np.asarray(rstd, dtype=np.float64)[:, None]
+    a_row = np.abs(w[None, :] * g * x).sum(axis=1, keepdims=True)
+    k_abs = rs ** 3 * a_row / H
+    val = np.abs(rs * w[None, :] * g) + k_abs * np.abs(x)
+    if res is not None:
+        val = val + np.abs(np.asarray(res, dtype=np.float64))
+    return U32 * (3.0 * val) + 110.0 * U32 * k_abs * np.abs(x)
+
+
+def rms_dx_violations(got, ref, fp32_err):
+    """Indices where |got - ref| > half a BF16 ulp of |ref| + err, plus twice
+    err (the rounded value can sit one BF16 step away only when ref is within
+    err of a rounding boundary)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = 0.5 * ulp_bf16(np.abs(ref) + fp32_err) + 2.0 * fp32_err
+    return np.argwhere(~(np.abs(got - ref) <= bound))
+
+
+def rms_dw_bound(abs_sum, T, S):
+    """Worst-case FP32 error of dw: a block's rows in sequence (at most
+    ceil(T / S) fused multiply-adds per column), then ceil(S / 8) block
+    partials per group and 8 groups, each step one rounding bounded by the
+    sum of |g x rstd|."""
+    depth = -(-T // S) + (-(-S // 8)) + 8 + 2
+    return depth * U32 * np.asarray(abs_sum, dtype=np.float64)
+
+
+def rms_schedule(T, H):
+    """Blocks S of the RMSNorm backward: min(ceil(T / 16), 256 P) with
+    P = max(1, 12 // ceil(H / 512)) (rows dealt round-robin)."""
+    if T == 0:
+        return 0
+    nc = -(-H // 512)
+    per = max(1, 12 // nc)
+    return min(-(-T // 16), 256 * per)
+
+
+def bf16_round_f64(v):
+    """FP64 values rounded once to the nearest BF16 (ties to even), as FP64:
+    8 significant bits, quantum at least 2^-133, beyond the range +-inf."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(v / q) * q
+    return np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, v), r)

@@ -292,3 +292,88 @@ def test_forward_validates_before_any_launch():
             m.mhcpb_plan_destroy(big)
     finally:
         m.mhcpb_plan_destroy(plan)
+
+
+# ---- BF16 RMSNorm backward -----------------------------------------------------
+
+def _rms_schedule(T, H):
+    nc = -(-H // 512)
+    return min(-(-T // 16), 256 * max(1, 12 // nc)) if T else 0
+
+
+@pytest.mark.parametrize("T,H,S", [(1, 5120, 1), (16, 5120, 1), (17, 5120, 2), (100, 5120, 7),
+                                   (4096, 5120, 256), (4097, 5120, 256), (16384, 5120, 256),
+                                   (16384, 6144, 256), (16384, 2048, 768), (16384, 256, 1024),
+                                   (65536, 512, 3072), (65536, 1536, 1024), (65536, 2560, 512)])
+def test_rmsnorm_blocks_depend_on_t_and_h_only(T, H, S):
+    assert _rms_schedule(T, H) == S
+    assert m.mhcpb_rmsnorm_backward_workspace_bytes(T, H) == S * H * 4
+
+
+@pytest.mark.parametrize("T,H,status", [(-1, 512, 1), (10, 0, 1), (10, -8, 1), (10, 4, 2),
+                                        (10, 12, 2), (10, 6152, 2), (2**31, 512, 2),
+                                        (0, 512, 0), (10, 6144, 0), (10, 8, 0)])
+def test_rmsnorm_shape_checks(T, H, status):
+    st, n = m.mhcpb_rmsnorm_backward_workspace_bytes(T, H, check=False)
+    assert st == status
+    if status == 0:
+        assert n == _rms_schedule(T, H) * H * 4
+
+
+class _FakeRms:
+    def __init__(self, T, H, w_f32=False):
+        S = _rms_schedule(T, H)
+        self.ws_needed = S * H * 4
+        sizes = dict(g=T * H * 2, x=T * H * 2, w=H * (4 if w_f32 else 2), rstd=T * 4,
+                     res=T * H * 2, dx=T * H * 2, dw=H * 4, ws=self.ws_needed)
+        base = 1 << 42
+        self.addr, self.size = {}, sizes
+        for k, n in sizes.items():
+            self.addr[k] = base
+            base += (n + 4095) // 4096 * 4096 + 4096
+
+    def call(self, T, H, ws_size=None, w_dtype=0, **over):
+        a = dict(self.addr)
+        a.update(over)
+        return m.mhcpb_rmsnorm_backward(T, H, a["g"], a["x"], a["w"], w_dtype, a["rstd"],
+                                        a["res"], a["dx"], a["dw"], a["ws"],
+                                        self.ws_needed if ws_size is None else ws_size, 0,
+                                        check=False)
+
+
+@fake_addresses
+def test_rmsnorm_validates_before_any_launch():
+    T, H = 64, 1024
+    f = _FakeRms(T, H)
+    for field in ("g", "x", "w", "rstd", "dx", "dw", "ws"):
+        assert f.call(T, H, **{field: None}) == m.MHCPB_ERROR_INVALID_ARGUMENT, field
+        for off in (2, 4, 8):
+            assert f.call(T, H, **{field: f.addr[field] + off}) == m.MHCPB_ERROR_MISALIGNED
+    assert f.call(T, H, res=f.addr["res"] + 8) == m.MHCPB_ERROR_MISALIGNED
+    assert f.call(T, H, w_dtype=2) == m.MHCPB_ERROR_INVALID_ARGUMENT
+    assert f.call(T, H, w_dtype=-1) == m.MHCPB_ERROR_INVALID_ARGUMENT
+    assert f.call(T, H, ws_size=f.ws_needed - 1) == m.MHCPB_ERROR_WORKSPACE
+    for a, b in (("g", "dx"), ("x", "res"), ("dw", "ws"), ("rstd", "w"), ("dx", "x"),
+                 ("res", "dw")):
+        over = {b: f.addr[a] + f.size[a] - 16}
+        assert f.call(T, H, **over) == m.MHCPB_ERROR_OVERLAP, (a, b)
+    # an FP32 weight is twice as long: overlapping only at its second half
+    f32 = _FakeRms(T, H, w_f32=True)
+    assert f32.call(T, H, w_dtype=1, dw=f32.addr["w"] + 2 * H) == m.MHCPB_ERROR_OVERLAP
+    assert f.call(T, 12) == m.MHCPB_ERROR_UNSUPPORTED
+    assert f.call(T, 6160) == m.MHCPB_ERROR_UNSUPPORTED
+
+
+@fake_addresses
+def test_rmsnorm_zero_rows_needs_only_w_and_dw():
+    f = _FakeRms(64, 512)
+    # T = 0: the row operands may be NULL, the workspace too (0 bytes)
+    st = m.mhcpb_rmsnorm_backward(0, 512, None, None, f.addr["w"], 0, None, None, None,
+                                  f.addr["dw"], None, 0, 0, check=False)
+    assert st == m.MHCPB_ERROR_LAUNCH  # validation passed; no GPU here to launch on
+    assert m.mhcpb_rmsnorm_backward(0, 512, None, None, None, 0, None, None, None,
+                                    f.addr["dw"], None, 0, 0, check=False) == \
+        m.MHCPB_ERROR_INVALID_ARGUMENT
+    assert m.mhcpb_rmsnorm_backward(0, 512, None, None, f.addr["w"], 0, None, None, None,
+                                    f.addr["w"] + 512, None, 0, 0, check=False) == \
+        m.MHCPB_ERROR_OVERLAP

@@ -166,3 +166,73 @@ def one_hot_rows(T: int, K: int, seed: int) -> torch.Tensor:
     x = torch.zeros(T, K, dtype=torch.float32)
     x[torch.arange(T), cols] = low_bit_values((T,), seed + 1)
     return x
+
+
+# ---- second workload: the BF16 RMSNorm backward --------------------------------
+# Inputs of the backward named on the
+# "flashinfer.cake_rmsnorm_det_train.cake_rmsnorm_det_train_backward" page:
+#
+#   g           BF16 [T, H], N(0, 1)  (the gradient of y; its scale does not
+#               matter for relative errors)
+#   x           BF16 [T, H], N(0, 1)  (the normalised input)
+#   w           [H], 1 + N(0, 0.1), BF16 or FP32 (a trained RMSNorm weight
+#               near its initial value 1)
+#   rstd        FP32 [T], (mean(x^2) + 1e-6)^(-1/2) of the BF16 x, computed in
+#               FP64 and rounded once (what the forward returns)
+#   g_residual  BF16 [T, H], N(0, 1), only where a workload has one
+#
+# The widths are the page's (256 ... 6144); 5120 is the hidden size of the
+# projection stage above, and T = 4096 and 16384 its token counts.
+
+@dataclass(frozen=True)
+class RmsWorkload:
+    name: str
+    T: int
+    H: int
+    seed: int
+    w_f32: bool = False
+    residual: bool = False
+
+
+RMS_WORKLOADS = {
+    w.name: w
+    for w in (
+        RmsWorkload("rms_small", 300, 1536, SEED_BASE + 20),
+        RmsWorkload("rms_train", 4096, 5120, SEED_BASE + 21),
+        RmsWorkload("rms_long", 16384, 5120, SEED_BASE + 22),
+        RmsWorkload("rms_residual", 4096, 6144, SEED_BASE + 23, residual=True),
+        RmsWorkload("rms_w32", 4096, 5120, SEED_BASE + 24, w_f32=True),
+    )
+}
+
+
+def rms_custom(T: int, H: int, seed: int = 1, w_f32: bool = False,
+               residual: bool = False) -> RmsWorkload:
+    return RmsWorkload(f"rms_T{T}_H{H}", T, H, seed, w_f32, residual)
+
+
+def rms_inputs(w: RmsWorkload, device="cpu") -> dict:
+    """Draw g, x, w, rstd (and g_residual) of ``w`` on the CPU, then move them
+    to ``device``; BF16 tensors are torch.bfloat16."""
+    gen = torch.Generator()
+    gen.manual_seed(w.seed)
+    T, H = w.T, w.H
+    g = torch.randn(T, H, generator=gen).to(torch.bfloat16)
+    x = torch.randn(T, H, generator=gen).to(torch.bfloat16)
+    wt = 1.0 + 0.1 * torch.randn(H, generator=gen)
+    wt = wt.to(torch.float32) if w.w_f32 else wt.to(torch.bfloat16)
+    rstd = rms_rstd(x)
+    res = torch.randn(T, H, generator=gen).to(torch.bfloat16) if w.residual else None
+    out = dict(g=g, x=x, w=wt, rstd=rstd, res=res)
+    return {k: (v.to(device) if v is not None else None) for k, v in out.items()}
+
+
+def rms_rstd(x: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+    """(mean(x^2) + eps)^(-1/2) per row of a BF16 x, in FP64, stored as FP32."""
+    rows = []
+    for i in range(0, x.shape[0], 1024):
+        xx = x[i:i + 1024].to(torch.float64)
+        rows.append(torch.rsqrt((xx * xx).mean(dim=1) + eps).to(torch.float32))
+    if not rows:
+        return torch.empty(0, dtype=torch.float32, device=x.device)
+    return torch.cat(rows)
