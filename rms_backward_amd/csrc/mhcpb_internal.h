@@ -88,14 +88,8 @@ hipError_t launch_forward(const Plan &p, const float *x, const float *w, float *
 // S = min(ceil(T / 16), 256 * P) and P = max(1, 12 / chunks) blocks per CU's
 // worth of waves: a function of (T, H) only, never of the device.  The
 // workspace holds one FP32 partial dw [H] per block.
-#ifndef MHCPB_RMS_MAX_BLOCKS
-#define MHCPB_RMS_MAX_BLOCKS 256
-#endif
-#ifndef MHCPB_RMS_MIN_ROWS
-#define MHCPB_RMS_MIN_ROWS 16
-#endif
-constexpr int64_t kRmsBlockUnit = MHCPB_RMS_MAX_BLOCKS;
-constexpr int64_t kRmsMinRowsPerBlock = MHCPB_RMS_MIN_ROWS;
+constexpr int64_t kRmsBlockUnit = 256;
+constexpr int64_t kRmsMinRowsPerBlock = 16;
 constexpr int kRmsChunkCols = 512;
 constexpr int kRmsWavesPerUnit = 12;
 constexpr int32_t kRmsMaxH = 6144;  // 12 chunks of 512 columns

@@ -45,10 +45,7 @@ namespace {
 #define MHCPB_CONST __attribute__((address_space(4)))
 
 constexpr int kRmsChunk = 512;  // columns per chunk: 64 lanes x 8 BF16
-#ifndef MHCPB_RMS_GROUP
-#define MHCPB_RMS_GROUP 8
-#endif
-constexpr int kRmsGroup = MHCPB_RMS_GROUP;  // rows a block takes at a time
+constexpr int kRmsGroup = 4;  // rows a block takes at a time
 constexpr int kReduceGroups = 8;  // kernel 2: block groups per column (one wave each)
 
 struct RmsArgs {

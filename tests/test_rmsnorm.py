@@ -203,3 +203,17 @@ def test_workspace_is_exactly_the_block_partials():
                      device=DEV)
     dx, dw = gh.run_rmsnorm(inp, workspace=ws)
     _check(inp, dx, dw, "exact workspace")
+
+
+def test_one_workspace_many_calls():
+    """One workspace serves calls of different shapes in turn, each giving the
+    bits of a call with a fresh workspace."""
+    import rms_backward_amd as m
+    shapes = [(4096, 5120), (300, 1536), (17, 6144), (4097, 520), (4096, 5120)]
+    need = max(m.mhcpb_rmsnorm_backward_workspace_bytes(T, H) for T, H in shapes)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    for i, (T, H) in enumerate(shapes):
+        inp = workloads.rms_inputs(workloads.rms_custom(T, H, seed=40 + i), DEV)
+        dx, dw = gh.run_rmsnorm(inp, workspace=ws)
+        dx_f, dw_f = gh.run_rmsnorm(inp)
+        assert torch.equal(dx, dx_f) and torch.equal(dw, dw_f), (T, H)
