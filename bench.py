@@ -552,7 +552,10 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed calls before the timed ones (default: about 50 ms of "
+                         "calls, enough for the GPU clocks to settle: 500 for the stage, "
+                         "600 for the forward, 2000 for the RMSNorm backward)")
     ap.add_argument("--workload", default="train")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows of the workload the CPU oracle baseline times")
@@ -567,6 +570,8 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter scaling)")
     args = ap.parse_args(argv)
+    if args.warmup is None:
+        args.warmup = {"backward": 500, "forward": 600, "rmsnorm": 2000}[args.stage]
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
