@@ -12,7 +12,8 @@ Checks, per case:
   significant bits, so both BF16 parts of every TF32 operand take part)
   against signs, whose sums stay below 2^24; one value per row, whose single
   product is exact, with random low bits and TF32 ties on both operands;
-* the pages' sizes (4096 and 16384 tokens, K = 20480) on sampled rows;
+* the pages' sizes (4095, 4096, 16384 and 65536 tokens, K = 20480) on
+  sampled rows;
 * every row's bits are independent of T and of the other rows, repeat runs
   and the event-timed form give the same bits;
 * non-finite and extreme rows.
@@ -98,7 +99,7 @@ def test_one_value_per_row_is_bit_exact(K, T):
     assert np.count_nonzero(got != ex_p) > got.size // 2
 
 
-@pytest.mark.parametrize("name", ["train", "long"])
+@pytest.mark.parametrize("name", ["train", "long", "large", "ragged"])
 def test_full_size_sampled(name):
     wl = workloads.WORKLOADS[name]
     inp = workloads.forward_inputs(wl, DEV)

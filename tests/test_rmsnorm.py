@@ -217,3 +217,32 @@ def test_one_workspace_many_calls():
         dx, dw = gh.run_rmsnorm(inp, workspace=ws)
         dx_f, dw_f = gh.run_rmsnorm(inp)
         assert torch.equal(dx, dx_f) and torch.equal(dw, dw_f), (T, H)
+
+
+@pytest.mark.parametrize("T,H,residual", [(65536, 5120, False), (65535, 6144, True)])
+def test_large_sampled(T, H, residual):
+    """65536 rows (and a ragged 65535 with g_residual): dx of sampled rows
+    against the oracle on those rows; dw of sampled columns against the
+    oracle on those columns (each column of dw depends on its own column
+    only, so a column-sliced oracle call gives it exactly)."""
+    wl = workloads.rms_custom(T, H, seed=T + H, residual=residual)
+    inp = workloads.rms_inputs(wl, DEV)
+    dx, dw = gh.run_rmsnorm(inp)
+    rng = np.random.default_rng(T)
+    rows = sorted({0, 1, 3, T // 2, T - 2, T - 1} | {int(v) for v in rng.integers(0, T, 58)})
+    _check(inp, dx, dw, f"large T{T} H{H} rows", rows=rows)
+    cols = torch.as_tensor(sorted({0, 7, 8, H - 1} | {int(v) for v in rng.integers(0, H, 252)}),
+                           device=DEV)
+    g_c = gh.bf16_bits_np(inp["g"].index_select(1, cols))
+    x_c = gh.bf16_bits_np(inp["x"].index_select(1, cols))
+    w_c = inp["w"].index_select(0, cols).float().cpu().numpy()
+    rstd = gh.host(inp["rstd"])
+    _, ref_dw = oracle.rmsnorm_backward(g_c, x_c, w_c, rstd)
+    got = gh.host(dw.index_select(0, cols)).astype(np.float64)
+    gx = mt.bf16_bits_to_f64(g_c) * mt.bf16_bits_to_f64(x_c)
+    abs_sum = (np.abs(gx) * rstd.astype(np.float64)[:, None]).sum(axis=0)
+    bound = mt.rms_dw_bound(abs_sum, T, mt.rms_schedule(T, H))
+    bad = np.argwhere(~(np.abs(got - ref_dw) <= bound))
+    print(f"large T{T} H{H}: dw frob {mt.rel_frobenius(got, ref_dw):.2e}, violations {len(bad)}")
+    assert len(bad) == 0
+    assert mt.rel_frobenius(got, ref_dw) <= 1e-6
