@@ -46,6 +46,7 @@ namespace {
 
 constexpr int kRmsChunk = 512;  // columns per chunk: 64 lanes x 8 BF16
 constexpr int kRmsGroup = 4;  // rows a block takes at a time
+constexpr uint64_t kRmsStreamBytes = 192ull << 20;
 constexpr int kReduceGroups = 8;  // kernel 2: block groups per column (one wave each)
 
 struct RmsArgs {
@@ -95,8 +96,11 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-template <int NC, bool WF32, bool RES>
+template <int NC, bool WF32, bool RES, bool NT>
 __global__ __launch_bounds__(NC * kWave) void rmsnorm_bwd_rows(RmsArgs a) {
+    // Cache policy of the row loads: non-temporal (nt) when the rows are
+    // streamed through once at sizes beyond the Infinity Cache.
+    constexpr int kLoadAux = NT ? 2 : 0;
     constexpr int R = kRmsGroup;
     // Per group: each chunk's sum of every row, double-buffered so that one
     // barrier per group suffices.
@@ -153,11 +157,11 @@ __global__ __launch_bounds__(NC * kWave) void rmsnorm_bwd_rows(RmsArgs a) {
         const bool ok = r < nrows;
         const int64_t t = blk + (ok ? r : 0) * S;
         const int nbytes = ok ? row_bytes : 0;
-        gv[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc32(a.g + t * H, nbytes), off, 0, 0);
-        xv[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc32(a.x + t * H, nbytes), off, 0, 0);
+        gv[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc32(a.g + t * H, nbytes), off, 0, kLoadAux);
+        xv[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc32(a.x + t * H, nbytes), off, 0, kLoadAux);
         if constexpr (RES)
             rv[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc32(a.res + t * H, nbytes), off,
-                                                          0, 0);
+                                                          0, kLoadAux);
         drs[r] = make_rsrc32(a.dx + t * H, nbytes);
         rs[r] = ok ? rstd_c[t] : 0.0f;
         // Issued in the order of the reloads below (row by row: g, x,
@@ -240,12 +244,12 @@ __global__ __launch_bounds__(NC * kWave) void rmsnorm_bwd_rows(RmsArgs a) {
             const int64_t t = blk + (ok ? kn : 0) * S;
             const int nbytes = ok ? row_bytes : 0;
             gv[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc32(a.g + t * H, nbytes), off, 0,
-                                                          0);
+                                                          kLoadAux);
             xv[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc32(a.x + t * H, nbytes), off, 0,
-                                                          0);
+                                                          kLoadAux);
             if constexpr (RES)
                 rv[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc32(a.res + t * H, nbytes),
-                                                              off, 0, 0);
+                                                              off, 0, kLoadAux);
             drs[r] = make_rsrc32(a.dx + t * H, nbytes);
             rs[r] = ok ? rstd_c[t] : 0.0f;
             __builtin_amdgcn_sched_barrier(0);
@@ -299,27 +303,32 @@ __global__ __launch_bounds__(kReduceGroups * kWave) void rmsnorm_dw_reduce(
 
 using RowsKernel = void (*)(RmsArgs);
 
-template <int NC>
-RowsKernel pick_rows(bool wf32, bool res) {
+template <int NC, bool NT>
+RowsKernel pick_nt(bool wf32, bool res) {
     if (wf32)
-        return res ? rmsnorm_bwd_rows<NC, true, true> : rmsnorm_bwd_rows<NC, true, false>;
-    return res ? rmsnorm_bwd_rows<NC, false, true> : rmsnorm_bwd_rows<NC, false, false>;
+        return res ? rmsnorm_bwd_rows<NC, true, true, NT> : rmsnorm_bwd_rows<NC, true, false, NT>;
+    return res ? rmsnorm_bwd_rows<NC, false, true, NT> : rmsnorm_bwd_rows<NC, false, false, NT>;
 }
 
-RowsKernel rows_kernel(int nc, bool wf32, bool res) {
+template <int NC>
+RowsKernel pick_rows(bool wf32, bool res, bool nt) {
+    return nt ? pick_nt<NC, true>(wf32, res) : pick_nt<NC, false>(wf32, res);
+}
+
+RowsKernel rows_kernel(int nc, bool wf32, bool res, bool nt) {
     switch (nc) {
-    case 1: return pick_rows<1>(wf32, res);
-    case 2: return pick_rows<2>(wf32, res);
-    case 3: return pick_rows<3>(wf32, res);
-    case 4: return pick_rows<4>(wf32, res);
-    case 5: return pick_rows<5>(wf32, res);
-    case 6: return pick_rows<6>(wf32, res);
-    case 7: return pick_rows<7>(wf32, res);
-    case 8: return pick_rows<8>(wf32, res);
-    case 9: return pick_rows<9>(wf32, res);
-    case 10: return pick_rows<10>(wf32, res);
-    case 11: return pick_rows<11>(wf32, res);
-    case 12: return pick_rows<12>(wf32, res);
+    case 1: return pick_rows<1>(wf32, res, nt);
+    case 2: return pick_rows<2>(wf32, res, nt);
+    case 3: return pick_rows<3>(wf32, res, nt);
+    case 4: return pick_rows<4>(wf32, res, nt);
+    case 5: return pick_rows<5>(wf32, res, nt);
+    case 6: return pick_rows<6>(wf32, res, nt);
+    case 7: return pick_rows<7>(wf32, res, nt);
+    case 8: return pick_rows<8>(wf32, res, nt);
+    case 9: return pick_rows<9>(wf32, res, nt);
+    case 10: return pick_rows<10>(wf32, res, nt);
+    case 11: return pick_rows<11>(wf32, res, nt);
+    case 12: return pick_rows<12>(wf32, res, nt);
     }
     return nullptr;
 }
@@ -333,7 +342,12 @@ hipError_t launch_rmsnorm_backward(const RmsPlan &p, const uint16_t *g, const ui
                                    hipEvent_t stop) {
     if (p.T > 0) {
         const int nc = rmsnorm_chunks(p.H);
-        RowsKernel k = rows_kernel(nc, w_f32, res != nullptr);
+        // Rows streamed through once: non-temporal loads once g, x (and
+        // g_residual) exceed about three quarters of the 256 MB Infinity
+        // Cache, which they would only thrash; smaller inputs may stay in it.
+        const uint64_t in_bytes = static_cast<uint64_t>(p.T) * static_cast<uint64_t>(p.H) * 2 *
+                                  (res != nullptr ? 3 : 2);
+        RowsKernel k = rows_kernel(nc, w_f32, res != nullptr, in_bytes >= kRmsStreamBytes);
         if (!k) return hipErrorInvalidValue;
         RmsArgs a{g, x, w, rstd, res, dx, ws, p.T, p.H};
         launch(k, dim3(static_cast<unsigned>(p.S)), dim3(nc * kWave), stream, start, mid, a);
