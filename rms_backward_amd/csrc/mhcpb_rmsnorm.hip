@@ -13,23 +13,25 @@
 //
 // dx is computed in FP32 and rounded to BF16 once (the residual added before
 // that rounding).  The same page's notes on reproducibility set the design
-// of dw: its rows are split into blocks whose number depends on T alone (never
-// on the CU count), and the block partials are added in a fixed order, so dw
-// is bitwise reproducible on any MI355X for a given (T, H), and dx of a row
-// depends on that row alone.
+// of dw: its rows are split into blocks whose number depends on (T, H) alone
+// (never on the CU count), and the block partials are added in a fixed
+// order, so dw is bitwise reproducible on any MI355X for a given (T, H), and
+// dx of a row depends on that row alone.
 //
 // Kernel 1 ("rows"): a block has one wave per 512-column chunk of a row
 // (every lane 8 columns, loaded as 16-byte vectors) and owns the rows b,
 // b + S, b + 2S, ... (S blocks; neighbouring blocks take neighbouring rows,
 // so the whole GPU sweeps the tensors front to back).  It takes its rows in
-// groups of R: each wave sums w g x over its chunk of each row (one wave
+// groups of R = 4: each wave sums w g x over its chunk of each row (one wave
 // reduction per row) and puts the R sums into LDS; after a barrier every
 // wave adds the chunks' sums of a row in chunk order, which gives the same
 // c1 in every wave, then writes its chunk of dx.  The wave's 8 weights and
 // 8 dw accumulators per lane stay in registers; at the end each wave writes
 // its columns of the block's FP32 partial dw [H] into the workspace.  While a
 // group is finished, the wave's registers of each row are reloaded with the
-// row R places later, so a wave keeps R rows of loads in flight.
+// row R places later, so a wave keeps R rows of loads in flight.  The row
+// loads are non-temporal when g, x (and g_residual) reach 192 MB, beyond
+// what the 256 MB Infinity Cache could keep.
 // Kernel 2 ("reduce") adds the S block partials in a fixed order: 8 groups
 // of consecutive blocks, each summed in ascending order, then the group sums
 // in group order.
