@@ -575,8 +575,8 @@ def main(argv=None):
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this stage is measured on one GPU only; runs on more than one "
-              "GPU are not part of this build (--gpus must be 1)", file=sys.stderr)
+        print("bench.py: the library runs on one GPU and is measured on one GPU only; "
+              "--gpus must be 1", file=sys.stderr)
         return 2
 
     import torch

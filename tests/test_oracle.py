@@ -1,7 +1,7 @@
 """Pins of the CPU oracle against what the pages and the mathematics fix.
 
-The oracle (oracle/mhcpb_oracle.c) is the definition the GPU library is judged
-by, so it is itself checked here against things other than its own code:
+The oracle (oracle/mhcpb_oracle.c) is the definition the GPU library is checked
+against, so it is itself checked here against things other than its own code:
 
 * the stage is the vector-Jacobian product of the forward map
   (X, W) -> (X W^T, r(X)), r(X) = sqrt(mean(X^2) + eps), for the cotangents
