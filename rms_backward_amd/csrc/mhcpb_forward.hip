@@ -498,17 +498,28 @@ __global__ __launch_bounds__(256) void forward_reduce(const float *__restrict__ 
     // floats of token t in tile 0; tile kt adds kt * tile_stride
     const int64_t base = (s * kFwdPairs + m / 2) * kWave + 32 * (m % 2);
     const int64_t tile_stride = static_cast<int64_t>(nsteps) * kFwdPairs * kWave;
+    // The squares and the logits of all tiles are requested together (one
+    // round trip), then added in tile order.  The thread of r (e == 6) reads
+    // floats 24..27 of the block as its "logits" and ignores them.
     float ss = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < nkt; k0 += kFwdReduceBatch) {
-        float v[kFwdReduceBatch];
+        float vs[kFwdReduceBatch];
+        f32x4 v[kFwdReduceBatch];
+#pragma unroll
+        for (int k = 0; k < kFwdReduceBatch; ++k) {
+            const bool in = k0 + k < nkt;
+            const float *blk = part + base + (k0 + k) * tile_stride;
+            vs[k] = in ? __builtin_nontemporal_load(blk + kProjCols) : 0.f;
+            v[k] = in ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(blk) + e)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int k = 0; k < kFwdReduceBatch; ++k)
-            v[k] = k0 + k < nkt
-                       ? __builtin_nontemporal_load(part + base + (k0 + k) * tile_stride + kProjCols)
-                       : 0.f;
-#pragma unroll
-        for (int k = 0; k < kFwdReduceBatch; ++k)
-            if (k0 + k < nkt) ss = (k0 + k == 0) ? v[k] : ss + v[k];
+            if (k0 + k < nkt) {
+                ss = (k0 + k == 0) ? vs[k] : ss + vs[k];
+                acc = (k0 + k == 0) ? v[k] : acc + v[k];
+            }
     }
     const float rv = __builtin_sqrtf(ss / static_cast<float>(K) + eps);
     const bool nan_row = rv != rv;
@@ -518,18 +529,6 @@ __global__ __launch_bounds__(256) void forward_reduce(const float *__restrict__ 
         out[kProjCols / 4 + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
         rout[t] = rv;
         return;
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < nkt; k0 += kFwdReduceBatch) {
-        f32x4 v[kFwdReduceBatch];
-#pragma unroll
-        for (int k = 0; k < kFwdReduceBatch; ++k)
-            v[k] = k0 + k < nkt ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
-                                      part + base + (k0 + k) * tile_stride) + e)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < kFwdReduceBatch; ++k)
-            if (k0 + k < nkt) acc = (k0 + k == 0) ? v[k] : acc + v[k];
     }
     const float qnan = __builtin_nanf("");
     out[e] = nan_row ? f32x4{qnan, qnan, qnan, qnan} : acc;
