@@ -32,7 +32,7 @@
 // row R places later, so a wave keeps R rows of loads in flight.  The row
 // loads are non-temporal when g, x (and g_residual) reach 192 MB, beyond
 // what the 256 MB Infinity Cache could keep.
-// Kernel 2 ("reduce") adds the S block partials in a fixed order: 8 groups
+// Kernel 2 ("reduce") adds the S block partials in a fixed order: 16 groups
 // of consecutive blocks, each summed in ascending order, then the group sums
 // in group order.
 //
@@ -49,7 +49,8 @@ namespace {
 constexpr int kRmsChunk = 512;  // columns per chunk: 64 lanes x 8 BF16
 constexpr int kRmsGroup = 4;  // rows a block takes at a time
 constexpr uint64_t kRmsStreamBytes = 192ull << 20;
-constexpr int kReduceGroups = 8;  // kernel 2: block groups per column (one wave each)
+constexpr int kReduceGroups = 16;  // kernel 2: block groups per column (one wave each)
+constexpr int kReduceBatch = 32;   // kernel 2: partials a lane requests before adding them
 
 struct RmsArgs {
     const uint16_t *g;
@@ -267,9 +268,10 @@ __global__ __launch_bounds__(NC * kWave) void rmsnorm_bwd_rows(RmsArgs a) {
 }
 
 // dw[h] = sum over the S block partials: group q (one wave) adds blocks
-// [q P, min(S, (q + 1) P)) in ascending order, P = ceil(S / 8), starting from
-// +0; the 8 group sums are then added in group order.  64 columns per
-// workgroup.
+// [q P, min(S, (q + 1) P)) in ascending order, P = ceil(S / 16), starting
+// from +0; the 16 group sums are then added in group order.  64 columns per
+// workgroup; a lane requests up to 32 partials before adding them, so a group
+// of up to 32 blocks costs one round trip to memory.
 __global__ __launch_bounds__(kReduceGroups * kWave) void rmsnorm_dw_reduce(
     const float *__restrict__ ws, float *__restrict__ dw, int S, int H) {
     __shared__ float sums[kReduceGroups][kWave];
@@ -281,16 +283,15 @@ __global__ __launch_bounds__(kReduceGroups * kWave) void rmsnorm_dw_reduce(
     const int b1 = (S < b0 + per) ? S : b0 + per;
     float acc = 0.0f;
     if (h < H) {
-        constexpr int kBatch = 8;
-        for (int b = b0; b < b1; b += kBatch) {
-            float v[kBatch];
+        for (int b = b0; b < b1; b += kReduceBatch) {
+            float v[kReduceBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
+            for (int u = 0; u < kReduceBatch; ++u)
                 v[u] = (b + u < b1) ? __builtin_nontemporal_load(
                                           ws + static_cast<int64_t>(b + u) * H + h)
                                     : -0.0f;
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) acc += v[u];
+            for (int u = 0; u < kReduceBatch; ++u) acc += v[u];
         }
     }
     sums[q][lane] = acc;

@@ -107,10 +107,10 @@ def rms_dx_violations(got, ref, fp32_err):
 
 def rms_dw_bound(abs_sum, T, S):
     """Worst-case FP32 error of dw: a block's rows in sequence (at most
-    ceil(T / S) fused multiply-adds per column), then ceil(S / 8) block
-    partials per group and 8 groups, each step one rounding bounded by the
+    ceil(T / S) fused multiply-adds per column), then ceil(S / 16) block
+    partials per group and 16 groups, each step one rounding bounded by the
     sum of |g x rstd|."""
-    depth = -(-T // S) + (-(-S // 8)) + 8 + 2
+    depth = -(-T // S) + (-(-S // 16)) + 16 + 2
     return depth * U32 * np.asarray(abs_sum, dtype=np.float64)
 
 
