@@ -62,8 +62,9 @@ typedef enum mhcpb_status {
  *   hidden  hidden size per stream; even, 2 <= hidden <= 2^20, so that every
  *           BF16 row of dX is a multiple of 16 bytes
  * Host work only: the split schedule, the grid and the workspace size.  The
- * split count S depends on T alone (S = min(32, ceil(T / 512))), which is
- * what makes dW bitwise reproducible across devices with different CU counts.
+ * split count S depends on T alone (S = min(32, max(ceil(T / 512),
+ * min(8, ceil(T / 64))))), which is what makes dW bitwise reproducible across
+ * devices with different CU counts.
  * On success *plan receives a new plan; on error *plan is set to NULL.
  */
 mhcpb_status_t mhcpb_plan_create(mhcpb_plan_t *plan, int64_t T, int32_t streams,

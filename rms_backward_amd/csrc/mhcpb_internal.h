@@ -12,12 +12,20 @@ constexpr int kProjCols = 24;    // columns of grad_proj that take part
 constexpr int kProjStride = 32;  // row length of grad_proj (8 ignored columns)
 constexpr int kMaxSplits = 32;
 constexpr int64_t kRowsPerSplit = 512;
+constexpr int kSmallSplits = 8;
+constexpr int64_t kSmallSplitRows = 64;
 
 // Split count as a function of T only: one partial dW slab per 512 tokens,
-// at most 32.  At T = 4096 this gives the 8 slabs whose FP32 [24, K] partials
-// make the 15,728,640-byte workspace of the page's supported profile.
+// at most 32, and below T = 4096 one slab per 64 tokens, up to eight (a slab
+// is walked in order by one wave per column group, so a short T in few slabs
+// would leave the GPU nearly idle).  At T = 4096 this gives the 8 slabs whose
+// FP32 [24, K] partials make the 15,728,640-byte workspace of the page's
+// supported profile.
 inline int32_t split_count(int64_t T) {
-    int64_t s = (T + kRowsPerSplit - 1) / kRowsPerSplit;
+    const int64_t big = (T + kRowsPerSplit - 1) / kRowsPerSplit;
+    const int64_t by_rows = (T + kSmallSplitRows - 1) / kSmallSplitRows;
+    const int64_t small = by_rows < kSmallSplits ? by_rows : kSmallSplits;
+    const int64_t s = big > small ? big : small;
     return static_cast<int32_t>(s > kMaxSplits ? kMaxSplits : s);
 }
 

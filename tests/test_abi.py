@@ -46,9 +46,10 @@ def test_workspace_at_supported_profile_matches_page():
         m.mhcpb_plan_destroy(plan)
 
 
-@pytest.mark.parametrize("T,expect", [(1, 1), (511, 1), (512, 1), (513, 2), (4095, 8),
-                                      (4096, 8), (4097, 9), (16383, 32), (16384, 32),
-                                      (65536, 32), (2**31 - 1, 32)])
+@pytest.mark.parametrize("T,expect", [(1, 1), (64, 1), (65, 2), (300, 5), (448, 7), (449, 8),
+                                      (511, 8), (512, 8), (513, 8), (4095, 8), (4096, 8),
+                                      (4097, 9), (16383, 32), (16384, 32), (65536, 32),
+                                      (2**31 - 1, 32)])
 def test_split_count_depends_on_T_only(T, expect):
     for hidden in (2, 512, 5120):
         plan = m.mhcpb_plan_create(T, 4, hidden)
