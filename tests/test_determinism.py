@@ -1,8 +1,9 @@
 """dW is bitwise reproducible: the partial sums are reduced in a fixed order
 with no atomics ("DSv4.1 mHC projection/RMS backward", introduction and
 "Source attribution"), and the split count depends on T only.  Repeated
-launches on the supported profile (4096 tokens, 4 streams x hidden 5120) and
-on 16384 tokens must give identical bits, as must dX."""
+launches on the supported profile (4096 tokens, 4 streams x hidden 5120), on
+16384 tokens and on the tiny profile (512 tokens, 8 slabs of 64 rows) must
+give identical bits, as must dX."""
 import pytest
 import torch
 
@@ -12,7 +13,7 @@ from tests import gpu_harness as gh
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,reps", [("train", 100), ("long", 20)])
+@pytest.mark.parametrize("name,reps", [("tiny", 100), ("train", 100), ("long", 20)])
 def test_repeated_launches_are_bitwise_identical(name, reps):
     wl = workloads.WORKLOADS[name]
     inp = workloads.make(wl, "cuda")

@@ -31,10 +31,14 @@ SMALL = [
     (3, 6, False, False),
     (16, 64, False, False),
     (17, 66, True, False),
-    (100, 128, False, True),
-    (513, 130, False, False),     # 2 slabs, ragged slab and column tile
-    (1100, 96, True, True),       # 3 slabs
-    (2049, 34, False, False),     # 5 slabs, K = 136 < one tile
+    (65, 10, False, False),       # 2 slabs of 33 and 32 rows: steps end inside a slab
+    (100, 128, False, True),      # 2 slabs of 50 rows
+    (300, 50, True, False),       # 5 slabs of 60 rows
+    (449, 20, False, False),      # 8 slabs of 57 rows, the last 50
+    (513, 130, False, False),     # 8 slabs of 65 rows (the last 58), ragged column tile
+    (1100, 96, True, True),       # 8 slabs of 138 rows, the last 134
+    (2049, 34, False, False),     # 8 slabs of 257 rows (the last 250), K = 136 < one tile
+    (4097, 8, False, False),      # 9 slabs of 456 rows, the last 449
 ]
 
 
@@ -99,7 +103,8 @@ def test_tiny_workload_every_element():
     dx, dw, ws, plan = gh.run(inp)
     h = gh.host_rows(inp, list(range(wl.T)))
     _check_dx(gh.bf16_bits_np(dx), h, wl.K, "tiny")
-    _check_dw(gh.host(dw), gh.host_cols(inp, list(range(wl.K))), 512, 1, "tiny")
+    S = mhcpb_plan_split_count(plan.handle)
+    _check_dw(gh.host(dw), gh.host_cols(inp, list(range(wl.K))), -(-wl.T // S), S, "tiny")
 
 
 @pytest.mark.parametrize("name", ["train", "ragged", "long", "addend", "large"])
