@@ -60,6 +60,39 @@ def test_split_count_depends_on_T_only(T, expect):
             m.mhcpb_plan_destroy(plan)
 
 
+def test_split_schedule_properties():
+    """Over every T up to 20000 and a sample beyond: S never decreases as T
+    grows, stays within 1..32, gives every slab at least one row (the kernel
+    takes rows [s L, min((s+1) L, T)) with L = ceil(T / S)), keeps the slabs
+    at 512 rows or fewer from T = 4096 up to the cap, and does not depend on
+    hidden."""
+    prev = 0
+    Ts = list(range(1, 20001)) + [2**k + d for k in range(15, 31) for d in (-1, 0, 1)]
+    for T in Ts:
+        plan = m.mhcpb_plan_create(T, 4, 2)
+        try:
+            S = m.mhcpb_plan_split_count(plan)
+        finally:
+            m.mhcpb_plan_destroy(plan)
+        L = -(-T // S)
+        assert 1 <= S <= 32 and S <= T, T
+        assert (S - 1) * L < T, f"T={T}: slab {S - 1} would be empty"
+        if T <= 20000:
+            assert S >= prev, T
+            prev = S
+        if 4096 <= T <= 32 * 512:
+            assert L <= 512, T
+    for T in (7, 300, 4096, 16385):
+        counts = set()
+        for hidden in (2, 64, 5120, 2**20):
+            plan = m.mhcpb_plan_create(T, 4, hidden)
+            try:
+                counts.add(m.mhcpb_plan_split_count(plan))
+            finally:
+                m.mhcpb_plan_destroy(plan)
+        assert len(counts) == 1, T
+
+
 @pytest.mark.parametrize("T,streams,hidden,status", [
     (0, 4, 512, m.MHCPB_ERROR_INVALID_ARGUMENT),
     (-5, 4, 512, m.MHCPB_ERROR_INVALID_ARGUMENT),
