@@ -135,8 +135,8 @@ mhcpb_status_t mhcpb_execute_with_events(
 
 /*
  * The split backward ("FP8 weight cache, split backward, fused mHC stream
- * gradient" on the prime-kernels page: the data gradient first, the weight
- * gradients after, so a caller can send dX on before dW is computed).  Each
+ * gradient" on the prime-kernels page: dX is produced by its own call, so
+ * that it can be handed on while dW is still to be computed).  Each
  * form reads X once, so the pair reads it twice; each output has exactly the
  * bits mhcpb_execute gives it.
  *
