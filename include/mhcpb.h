@@ -10,11 +10,11 @@
  *
  * over X of shape [T, K], K = streams * hidden.  Both matrix products round
  * their operands to TF32 (round to nearest even of the FP32 fraction at 10
- * bits) and accumulate in FP32; the RMS term is FP32 arithmetic on the raw x.
- * dW is reduced from per-slab partial sums in a fixed order without atomics,
- * so its bits depend only on (T, K) and this library, never on the CU count,
- * the launch timing or the run.  Outputs are overwritten, not accumulated
- * (same page, introduction).
+ * bits) and sum in FP32; the RMS term is computed in FP32 from the raw x.
+ * dW is the sum of per-slab partial sums added in an order fixed in advance,
+ * with no atomic operations, so its bits depend only on (T, K) and this
+ * library, never on the CU count, the launch timing or the run.  dX and dW
+ * are written, never added to (same page, introduction).
  *
  * Tensor contract (same page, "Requirements and tensor contract"): compact
  * row-major tensors, columns 24..31 of grad_proj are never read, r holds the

@@ -3,7 +3,7 @@
 // Follows the "Prepared class API" and "Requirements and tensor contract"
 // sections of the "DSv4.1 mHC projection/RMS backward" page: a plan is host
 // metadata; execute() checks the operands (alignment, disjointness), then
-// enqueues exactly two kernels and allocates nothing.  The split forms (dX
+// puts the two kernels on the stream and allocates no memory.  The split forms (dX
 // only, dW only) follow the split backward of the prime-kernels page ("FP8
 // weight cache, split backward, fused mHC stream gradient").  The forward
 // entry points (the map the stage differentiates) use the same plan.
