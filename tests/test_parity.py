@@ -97,6 +97,28 @@ def test_small_shapes_every_element(T, hidden, addend, rescale):
     _check_dw(gh.host(dw), dict(x=h["x"], grad_proj=h["grad_proj"]), L, S, label)
 
 
+def _random_shapes(n, seed=20261203):
+    """Seeded (T, hidden, addend, rescale) draws: T from 1 to 3000, uniform and
+    log-uniform in turn (split counts 1 to 8, ragged last steps and slabs),
+    hidden even from 2 to 700 (K from 8 to 2800: ragged column tiles, K below
+    one wave's columns)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        if i % 2:
+            T = max(1, int(round(float(np.exp(rng.uniform(0.0, np.log(3000.0)))))))
+        else:
+            T = int(rng.integers(1, 3001))
+        hidden = 2 * int(rng.integers(1, 351))
+        out.append((T, hidden, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("T,hidden,addend,rescale", _random_shapes(20))
+def test_random_shapes_every_element(T, hidden, addend, rescale):
+    test_small_shapes_every_element(T, hidden, addend, rescale)
+
+
 def test_tiny_workload_every_element():
     wl = workloads.WORKLOADS["tiny"]
     inp = workloads.make(wl, "cuda")
