@@ -66,6 +66,26 @@ def test_small_shapes_every_element(T, hidden):
     _check_random(gh.host(proj), gh.host(r), ref_p, ref_r, wl.K, f"T{T} h{hidden}")
 
 
+def _random_shapes(n, seed=20261204):
+    """Seeded (T, hidden) draws: T from 1 to 2000, uniform and log-uniform in
+    turn; hidden even from 2 to 1400 (K up to 5600: one to six 1024-column
+    tiles, ragged in every position)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        if i % 2:
+            T = max(1, int(round(float(np.exp(rng.uniform(0.0, np.log(2000.0)))))))
+        else:
+            T = int(rng.integers(1, 2001))
+        out.append((T, 2 * int(rng.integers(1, 701))))
+    return out
+
+
+@pytest.mark.parametrize("T,hidden", _random_shapes(12))
+def test_random_shapes_every_element(T, hidden):
+    test_small_shapes_every_element(T, hidden)
+
+
 @pytest.mark.parametrize("K,T", [(20480, 64), (4120, 33), (2048, 40)])
 def test_integers_are_exact(K, T):
     """Odd integers against signs, both ways round: every partial sum is an
