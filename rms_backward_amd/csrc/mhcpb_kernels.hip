@@ -338,6 +338,14 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     // The ready count of a step's slot is read one step early, so that its
     // round trip is off the step's critical path.
     uint32_t ready_seen = lds_read_u32(ready_addr);
+    // With the addend, the dX stores of a step are issued one step late,
+    // right after the next X request (same bits; at T = 16384 with the
+    // addend 466 against 475 us, while without it they cost about 2 us at
+    // T = 4096, so only this form defers them).
+    constexpr bool kDefer = kAddend && kDX;
+    uint32_t pend[4][2] = {};
+    char *d_prev = d_cur;
+    int d_range_prev = 0;
     for (int j = 0; j < nsteps; ++j) {
         const int rows_left = slab_rows - kStepRows * j;
         // From the top of the step until the next X is requested the wave
@@ -373,16 +381,19 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         }
         // Then wait for this step's X and read it (4 rows).  Step j >= 1
         // issues, in this order: [4 addend loads] 4 X DMA (for step j + 1),
-        // [4 dX stores]; step 0 issues no X (the prologue requested steps 0
-        // and 1, after the W loads).  So after the X of step j come at most
-        // the stores of step j - 1 (4, or none without dX), and after the X
-        // of step 0 the X of step 1: vmcnt(4), or vmcnt(0) for the later
-        // steps of the dW-only form, covers it.  For step 1 with the addend,
-        // step 0's addend loads come after the X of step 1 as well, and the
-        // wait is only stricter.  Steps past the slab end are still requested
-        // (they read zeros; their stores fall outside the range), which keeps
-        // every step's count identical.
-        if (kDX || j == 0)
+        // [4 dX stores of step j - 1 when deferred], [4 dX stores of step j
+        // otherwise]; step 0 issues no X (the prologue requested steps 0 and
+        // 1, after the W loads).  So after the X of step j come at most 4
+        // stores (of step j - 1, or of step j - 2 when deferred; none without
+        // dX), and after the X of step 0 the X of step 1: vmcnt(4), or
+        // vmcnt(0) for the later steps of the dW-only form, covers it.  With
+        // deferred stores step 0 stores nothing, so step 1 waits for
+        // vmcnt(0).  For step 1 with the addend, step 0's addend loads come
+        // after the X of step 1 as well, and the wait is only stricter.
+        // Steps past the slab end are still requested (they read zeros;
+        // their stores fall outside the range), which keeps every step's
+        // count identical.
+        if (j == 0 || (kDX && !(kDefer && j == 1)))
             wait_vmcnt<4>();
         else
             wait_vmcnt<0>();
@@ -425,6 +436,14 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         }
         compiler_fence();
         __builtin_amdgcn_s_setprio(0);
+        if (kDefer && j > 0) {
+            const __amdgpu_buffer_rsrc_t prs = make_rsrc32(d_prev, d_range_prev);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{pend[rr][0], pend[rr][1]}, prs,
+                                                      doff[rr], 0, MHCPB_DX_AUX);
+        }
+        compiler_fence();
 
         const float ce[4] = {cc[0], cc[1], cc[2], cc[3]};
         u32x4 pb[2][2];
@@ -480,7 +499,15 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         }
         // One rounding to BF16 per element (above), then 8-byte range-checked
         // stores: rows past the slab end are dropped.
-        if constexpr (kDX) {
+        if constexpr (kDefer) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                pend[rr][0] = packed[rr][0];
+                pend[rr][1] = packed[rr][1];
+            }
+            d_prev = d_cur;
+            d_range_prev = d_range;
+        } else if constexpr (kDX) {
             const __amdgpu_buffer_rsrc_t drs = make_rsrc32(d_cur, d_range);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
@@ -489,6 +516,13 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         }
         d_cur += kStepRows * row_bytes_d;
         ready_seen = lds_read_u32(ready_addr + 4 * ((j + 1) % kSlots));
+    }
+    if (kDefer && nsteps > 0) {  // the last step's stores
+        const __amdgpu_buffer_rsrc_t prs = make_rsrc32(d_prev, d_range_prev);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pend[rr][0], pend[rr][1]}, prs, doff[rr],
+                                                  0, MHCPB_DX_AUX);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ready_seen)::"memory");
     // Drain the X DMA still in flight (the step past the slab end) before
