@@ -114,6 +114,17 @@ constexpr int kRawBufs = kRawAhead + 1;
 //
 // Two workgroups per CU make 12 waves (NW = 5), three per SIMD: the register
 // allocation must stay within 168 VGPRs.
+// A pointer the compiler may have kept in vector registers, as the uniform
+// value it is (from the first lane).  The deferred dX stores take their
+// buffer resource from values carried across loop iterations; without this
+// the compiler wrapped each such store in a loop over distinct resources.
+__device__ __forceinline__ char *uniform_ptr(char *p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    return reinterpret_cast<char *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int NW, bool kAddend, bool kDX, bool kDW>
 __global__ __launch_bounds__((NW + 1) * kWave)
 __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
@@ -437,7 +448,8 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         compiler_fence();
         __builtin_amdgcn_s_setprio(0);
         if (kDefer && j > 0) {
-            const __amdgpu_buffer_rsrc_t prs = make_rsrc32(d_prev, d_range_prev);
+            const __amdgpu_buffer_rsrc_t prs =
+                make_rsrc32(uniform_ptr(d_prev), __builtin_amdgcn_readfirstlane(d_range_prev));
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{pend[rr][0], pend[rr][1]}, prs,
@@ -518,7 +530,8 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         ready_seen = lds_read_u32(ready_addr + 4 * ((j + 1) % kSlots));
     }
     if (kDefer && nsteps > 0) {  // the last step's stores
-        const __amdgpu_buffer_rsrc_t prs = make_rsrc32(d_prev, d_range_prev);
+        const __amdgpu_buffer_rsrc_t prs =
+            make_rsrc32(uniform_ptr(d_prev), __builtin_amdgcn_readfirstlane(d_range_prev));
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{pend[rr][0], pend[rr][1]}, prs, doff[rr],
