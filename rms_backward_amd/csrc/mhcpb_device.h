@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <tuple>
 
 namespace mhcpb {
 namespace {
@@ -183,29 +184,48 @@ __device__ __forceinline__ void lds_signal(uint32_t addr, int lane) {
     if (lane == 0) asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(1u) : "memory");
 }
 
-// Waits until the LDS counter at addr is at least target.  The callers'
-// counters always get there, within a few steps' time; the bound (2^16
-// polls, a few milliseconds) only keeps a broken invariant from hanging the
-// GPU.
-constexpr int kMaxPolls = 1 << 16;
-__device__ __forceinline__ void lds_wait_at_least(uint32_t addr, uint32_t target) {
-    for (int poll = 0; poll < kMaxPolls; ++poll) {
+// Waits until the LDS counter at addr is at least target, polling at most
+// max_polls times; returns false if it gave up.  The callers' counters always
+// get there, within a few steps' time; the bound (2^16 polls by default, a
+// few milliseconds) only keeps a broken invariant from hanging the GPU, and a
+// caller whose wait gives up marks what it writes from then on as
+// untrustworthy (NaN outputs).  With max_polls = 0 every wait gives up at
+// once, which is how the tests reach that path.
+__device__ __forceinline__ bool lds_wait_at_least(uint32_t addr, uint32_t target, int max_polls) {
+    for (int poll = 0; poll < max_polls; ++poll) {
         uint32_t v;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-        if (__builtin_amdgcn_readfirstlane(v) >= target) return;
+        if (__builtin_amdgcn_readfirstlane(v) >= target) return true;
         __builtin_amdgcn_s_sleep(1);
     }
+    return false;
+}
+
+// Sets the workgroup's LDS poison word at addr (lane 0 writes it) and waits
+// until the write has completed, so that LDS accesses issued afterwards by
+// this wave come after it.
+__device__ __forceinline__ void lds_raise_poison(uint32_t addr, int lane) {
+    if (lane == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(1u) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // A launch with the given events attached to the dispatch (start and end
-// times), or a plain launch when both are null.
+// times), or a plain launch when both are null.  Returns the status of this
+// launch alone (the runtime's return value, not the thread's last error, which
+// could be left over from unrelated earlier work).
 template <typename... KArgs, typename... Args>
-void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start,
-            hipEvent_t stop, Args... args) {
-    if (start || stop)
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, args...);
-    else
-        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                  hipEvent_t start, hipEvent_t stop, Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    std::tuple<KArgs...> values(static_cast<KArgs>(args)...);
+    void *ptrs[sizeof...(KArgs)];
+    std::apply([&](auto &...v) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void *>(&v)), ...);
+    }, values);
+    const void *fn = reinterpret_cast<const void *>(kernel);
+    if (start || stop) return hipExtLaunchKernel(fn, grid, block, ptrs, 0, stream, start, stop, 0);
+    return hipLaunchKernel(fn, grid, block, ptrs, 0, stream);
 }
 
 }  // namespace

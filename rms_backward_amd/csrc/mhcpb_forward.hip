@@ -121,6 +121,8 @@ struct FwdCtx {
     uint32_t ring;   // LDS address of this wave's X ring
     uint32_t slots;  // LDS address of the reduction slots
     uint32_t ready, consumed;
+    uint32_t poison;  // LDS word raised by a wave whose bounded wait gave up
+    int max_polls;    // bound of the counter waits
 };
 
 // A unit of the workgroup's run: tile kt, 16-token step s (first token
@@ -251,11 +253,14 @@ __device__ __forceinline__ void fwd_reduce(const FwdCtx &c, int i, const FwdUnit
     constexpr int kPairsPerWave = kFwdPairs / NW;
     const int col = c.lane % 32;
     float sum[kPairsPerWave], ssum[kPairsPerWave];
+    bool poisoned = false;
 #pragma unroll
     for (int j = 0; j < kPairsPerWave; ++j) sum[j] = ssum[j] = 0.f;
     if (i >= 0) {
         const int slot = i % kFwdSlots;
-        lds_wait_at_least(c.ready + 4 * slot, NW * static_cast<uint32_t>(i / kFwdSlots + 1));
+        if (!lds_wait_at_least(c.ready + 4 * slot, NW * static_cast<uint32_t>(i / kFwdSlots + 1),
+                                c.max_polls))
+            lds_raise_poison(c.poison, c.lane);
         const int b = col / 16, nn = col % 16;
         float v[kPairsPerWave][NW], sv[kPairsPerWave][NW];
 #pragma unroll
@@ -269,12 +274,16 @@ __device__ __forceinline__ void fwd_reduce(const FwdCtx &c, int i, const FwdUnit
                 sv[j][ww] = lds_read_f32(ssrc + ww * (kFwdRows * 4));
             }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // The poison word is read after the slot: a wave that gave up
+        // raised it before it overwrote a slot.
+        uint32_t pois = lds_read_u32(c.poison);
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(pois)::"memory");
 #pragma unroll
         for (int j = 0; j < kPairsPerWave; ++j)
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww)
                 asm volatile("" : "+v"(v[j][ww]), "+v"(sv[j][ww]));
+        poisoned = __builtin_amdgcn_readfirstlane(pois) != 0;
         lds_signal(c.consumed + 4 * slot, c.lane);
 #pragma unroll
         for (int j = 0; j < kPairsPerWave; ++j) {
@@ -291,7 +300,10 @@ __device__ __forceinline__ void fwd_reduce(const FwdCtx &c, int i, const FwdUnit
     for (int j = 0; j < kPairsPerWave; ++j) {
         const float low = __shfl_xor(sum[j], 8);  // column + 8: the low part
         if (col >= 16 && col < 24) sum[j] += low;
-        const float out = col < kProjCols ? sum[j] : (col == kProjCols ? ssum[j] : 0.f);
+        // After a give-up the sums of squares become NaN, which makes the
+        // token's r and all its logits NaN in kernel 2.
+        const float ssv = poisoned ? __builtin_nanf("") : ssum[j];
+        const float out = col < kProjCols ? sum[j] : (col == kProjCols ? ssv : 0.f);
         const int p = c.wave * kPairsPerWave + j;
         const int64_t blk = (static_cast<int64_t>(un.kt) * c.nsteps + un.s) * kFwdPairs + p;
         const i32x4 brs = rsrc_words(c.part + blk * kWave, i >= 0 ? kWave * 4 : 0);
@@ -376,13 +388,13 @@ __device__ __forceinline__ void fwd_steps(const FwdCtx &c, bool first, int &stag
 template <int NW>
 __global__ __launch_bounds__(NW * kWave) void forward_tiles(
     const float *__restrict__ x, const float *__restrict__ w, float *__restrict__ part, int64_t T,
-    int64_t K, int units, int upw, int nsteps) {
+    int64_t K, int units, int upw, int nsteps, int max_polls) {
     constexpr int NG = kFwdTileCols / (32 * NW);  // 32-column groups per wave
     constexpr int SPU = NG / 2;                   // steps per unit
     static_assert(NG % 2 == 0 && SPU >= 2, "at least two steps per unit");
     __shared__ f32x4 xring[NW][kFwdStages][kFwdDma][kWave];
     __shared__ FwdSlot<NW> slots[kFwdSlots];
-    __shared__ uint32_t ready[kFwdSlots], consumed[kFwdSlots];
+    __shared__ uint32_t ready[kFwdSlots], consumed[kFwdSlots], poison[1];
     FwdCtx c;
     c.x = x;
     c.w = w;
@@ -401,10 +413,13 @@ __global__ __launch_bounds__(NW * kWave) void forward_tiles(
     c.slots = lds_addr(&slots[0]);
     c.ready = lds_addr(&ready[0]);
     c.consumed = lds_addr(&consumed[0]);
+    c.poison = lds_addr(&poison[0]);
+    c.max_polls = max_polls;
     if (threadIdx.x < kFwdSlots) {
         lds_write_u32(c.ready + 4 * threadIdx.x, 0u);
         lds_write_u32(c.consumed + 4 * threadIdx.x, 0u);
     }
+    if (threadIdx.x == 0) lds_write_u32(c.poison, 0u);
     lds_barrier();
 
     // DMA offsets of this lane (see fwd_issue_x) and the A-operand reads:
@@ -456,7 +471,9 @@ __global__ __launch_bounds__(NW * kWave) void forward_tiles(
         ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
         const int slot = i % kFwdSlots;
-        lds_wait_at_least(c.consumed + 4 * slot, NW * static_cast<uint32_t>(i / kFwdSlots));
+        if (!lds_wait_at_least(c.consumed + 4 * slot, NW * static_cast<uint32_t>(i / kFwdSlots),
+                                c.max_polls))
+            lds_raise_poison(c.poison, c.lane);
         lds_write_u128(fwd_slot_acc<NW>(c, slot, c.wave, 0, c.lane), __builtin_bit_cast(u32x4, acc0));
         lds_write_u128(fwd_slot_acc<NW>(c, slot, c.wave, 1, c.lane), __builtin_bit_cast(u32x4, acc1));
         if (c.lane < kFwdRows)
@@ -553,8 +570,9 @@ hipError_t launch_forward(const Plan &p, const float *x, const float *w, float *
     const int units = static_cast<int>(units64);  // < 2^31: checked before the launch
     const int upw = (units + kGrid - 1) / kGrid;
     const int grid = (units + upw - 1) / upw;
-    launch(forward_tiles<NW>, dim3(grid), dim3(NW * kWave), stream, start, mid, x, w, ws, p.T,
-           p.K, units, upw, nsteps);
+    const hipError_t e = launch(forward_tiles<NW>, dim3(grid), dim3(NW * kWave), stream, start,
+                                mid, x, w, ws, p.T, p.K, units, upw, nsteps, p.wait_polls);
+    if (e != hipSuccess) return e;
     // Kernel 2: 256 threads per block, or 128 where 256 would give fewer
     // blocks than CUs (below about 9400 tokens): the reduce is bound by the
     // latency of its loads, and at 4096 tokens the smaller blocks spread it
@@ -562,9 +580,8 @@ hipError_t launch_forward(const Plan &p, const float *x, const float *w, float *
     const int64_t threads = p.T * (kProjCols / 4 + 1);
     const int64_t bs = (threads + 255) / 256 < 256 ? 128 : 256;
     const unsigned blocks = static_cast<unsigned>((threads + bs - 1) / bs);
-    launch(forward_reduce, dim3(blocks), dim3(static_cast<unsigned>(bs)), stream, nullptr, stop, ws,
-           proj, r, p.T, nkt, nsteps, p.K, eps);
-    return hipGetLastError();
+    return launch(forward_reduce, dim3(blocks), dim3(static_cast<unsigned>(bs)), stream, nullptr,
+                  stop, ws, proj, r, p.T, nkt, nsteps, p.K, eps);
 }
 
 }  // namespace mhcpb

@@ -37,7 +37,16 @@ struct Plan {
     int32_t S;        // splits (partial dW slabs)
     int64_t L;        // rows per slab, ceil(T / S); the last slab may be shorter
     size_t ws_bytes;  // S * 24 * K * 4
+    int32_t wait_polls;  // bound of the kernels' LDS counter waits
 };
+
+// Default bound of the kernels' LDS counter waits (polls of a few dozen
+// cycles each), and the environment variable that overrides it for a plan
+// created while it is set: a decimal in [0, 2^20].  0 makes every wait give
+// up at once, so that the tests can reach the path on which the kernels turn
+// the results they write into NaN.
+constexpr int32_t kDefaultWaitPolls = 1 << 16;
+constexpr const char *kWaitPollsEnv = "MHCPB_WAIT_POLLS";
 
 struct Args {
     const float *x;
@@ -62,6 +71,7 @@ hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStrea
 // Kernel 2: dW = sum of the S slabs in ascending order; the optional event
 // takes the end time of the dispatch.
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop);
+
 
 // Forward: the K columns are cut into tiles of kFwdTileCols; kernel 1
 // writes one partial (24 logits and a sum of squares) per tile and token into

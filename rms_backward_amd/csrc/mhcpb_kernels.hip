@@ -80,20 +80,36 @@ constexpr int kSlots = 4;
 constexpr int kRawAhead = 2;
 constexpr int kRawBufs = kRawAhead + 1;
 
-// Kernel 1.  A workgroup has NW compute waves, which own NW * 64 columns of
-// one slab, and one producer wave.  Per step a compute wave handles 16 rows x
-// 64 columns: lane l (c = l % 16, g = l / 16) holds x[t0 + 4g + r][kw + 4c + i]
-// for r, i in 0..3.
+// Kernel 1.  A workgroup has NW compute waves, which own the NW * 64 columns
+// of one column tile, and one producer wave.  The workgroup walks, one after
+// the other, the slabs s = sg, sg + G, sg + 2G, ... < S of its tile (sg = its
+// slab group): one unit of work per slab, each unit's rows in ascending
+// 16-row steps, and the steps of all its units form one continuous sequence
+// (global step k).  Per step a compute wave handles 16 rows x 64 columns:
+// lane l (c = l % 16, g = l / 16) holds x[t0 + 4g + r][kw + 4c + i] for r, i
+// in 0..3.
 //  dX: C_i[e] = dX[t0 + 4g + e][kw + 4c + i] = c_t x + the products of the P
 //      parts (token t0 + l%16) with the W parts (column kw + 4c + i): per
 //      MFMA (P part p, j block b) lane group g covers j = 16b + 4g .. +3 times
 //      (W hi, W lo); 4 MFMAs cover the 96 products of 24 j (8 padded).
-//  dW: acc[i][b][e] = sum over tokens of TF32(x) of column kw + 4(4g+e) + i
-//      times TF32(P[j]), j = 16 b + l%16: per MFMA (P part p), lane group g
-//      covers rows 4g .. 4g+3 times (x hi, x lo).
+//  dW: acc[i][b][e] = sum over the slab's tokens of TF32(x) of column
+//      kw + 4(4g+e) + i times TF32(P[j]), j = 16 b + l%16: per MFMA (P part
+//      p), lane group g covers rows 4g .. 4g+3 times (x hi, x lo).  At the
+//      end of each unit the 24 x 64 partial goes to workspace slab s and the
+//      accumulators restart from zero.
+//
+// Why one workgroup walks several slabs: a workgroup needs 6 waves and
+// 75 KB of LDS, so a CU holds one at a time; with one workgroup per (tile,
+// slab) the supported profile (64 tiles x 8 slabs) ran as two rounds of 256
+// workgroups, each with its own start-up (the first X and W requests) and
+// drain.  With G = 4 slab groups the 256 workgroups each stream two slabs
+// back to back: the X of the next unit is requested while the last step of
+// the current one is computed and its partial is stored.  A column's dW sums
+// the same rows in the same order whatever the grouping, so the grouping
+// changes no bit of the result.
 //
 // Memory pipeline.  Each compute wave streams its X through a two-step ring
-// in LDS: the DMA for step j + 1 is issued as soon as step j has arrived, so
+// in LDS: the DMA for step k + 1 is issued as soon as step k has arrived, so
 // one step per wave is in flight.  The producer wave copies the raw P of step
 // k into LDS (DMA) two steps ahead, converts it into operand slot k % 4 and
 // publishes it; it never touches X.
@@ -106,14 +122,17 @@ constexpr int kRawBufs = kRawAhead + 1;
 // read step k - 4 from the slot.  A slot's next use needs the previous one
 // consumed by every wave, so the counts identify the use exactly, and every
 // wait refers to an event of an earlier step, so none can deadlock.  The
-// waits are also bounded, so a broken invariant cannot hang the GPU.  Compute
-// waves never wait for each other.
+// waits are also bounded, so a broken invariant cannot hang the GPU; a wave
+// whose wait gives up raises the workgroup's poison word, and from then on
+// every dX value and dW partial the workgroup writes is NaN (the results
+// computed after a give-up could come from stale or overwritten operands).
+// Compute waves never wait for each other.
 //
 // kDX and kDW select the outputs: both (the fused stage), dX only or dW only
 // (the split forms); the arithmetic of each output is the same in every form.
 //
-// Two workgroups per CU make 12 waves (NW = 5), three per SIMD: the register
-// allocation must stay within 168 VGPRs.
+// A CU holds one workgroup (six waves, at most two per SIMD), so a wave may
+// use up to 256 VGPRs.
 // A pointer the compiler may have kept in vector registers, as the uniform
 // value it is (from the first lane).  The deferred dX stores take their
 // buffer resource from values carried across loop iterations; without this
@@ -125,48 +144,89 @@ __device__ __forceinline__ char *uniform_ptr(char *p) {
     return reinterpret_cast<char *>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// Position in a workgroup's sequence of steps: unit u (slab sg + u G), step j
+// of that slab, the slab's first row and row count, and its step count.  Past
+// the last unit the slab has no rows, so every request of such a step falls
+// outside its buffer range.
+struct StepCursor {
+    int u;
+    int j;
+    int nst;        // steps of the current slab
+    int slab_rows;  // rows of the current slab (0 past the last unit)
+    int64_t row0;   // first row of the current slab
+};
+
+__device__ __forceinline__ int slab_rows_at(int64_t row0, int64_t L, int64_t T) {
+    const int64_t n = T - row0 < L ? T - row0 : L;
+    return static_cast<int>(n > 0 ? n : 0);
+}
+
+__device__ __forceinline__ StepCursor cursor_start(int sg, int64_t L, int64_t T) {
+    StepCursor c;
+    c.u = 0;
+    c.j = 0;
+    c.row0 = static_cast<int64_t>(sg) * L;
+    c.slab_rows = slab_rows_at(c.row0, L, T);
+    c.nst = (c.slab_rows + 15) / 16;
+    return c;
+}
+
+// Advances by one step; returns true when the step left was the last of its
+// unit.
+__device__ __forceinline__ bool cursor_next(StepCursor &c, int G, int64_t L, int64_t T) {
+    if (++c.j < c.nst) return false;
+    c.j = 0;
+    ++c.u;
+    c.row0 += static_cast<int64_t>(G) * L;
+    c.slab_rows = slab_rows_at(c.row0, L, T);
+    c.nst = (c.slab_rows + 15) / 16;
+    return true;
+}
+
+// Number of store instructions of one partial dW write (per compute wave).
+constexpr int kPartialStores = 6;
+
 template <int NW, bool kAddend, bool kDX, bool kDW>
 __global__ __launch_bounds__((NW + 1) * kWave)
-__attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
+__attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
     const float *__restrict__ x, const float *__restrict__ w,
     const float *__restrict__ grad_proj, const float *__restrict__ grad_r,
     const float *__restrict__ r, uint16_t *__restrict__ dx, float *__restrict__ ws,
-    const uint16_t *__restrict__ addend, int64_t T, int64_t K, int64_t L) {
+    const uint16_t *__restrict__ addend, int64_t T, int64_t K, int64_t L, int S, int tiles,
+    int G, int max_polls) {
     __shared__ f32x4 xring[NW][2][4][kWave];
     __shared__ RawStep praw[kRawBufs];
     __shared__ StepP pop[kSlots];
-    __shared__ uint32_t ready[kSlots], consumed[kSlots];
+    __shared__ uint32_t ready[kSlots], consumed[kSlots], poison[1];
     constexpr int kThreads = (NW + 1) * kWave;
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int c16 = lane % 16;
     const int g = lane / 16;
-    const int s = blockIdx.y;
-    const int64_t row0 = static_cast<int64_t>(s) * L;
-    const int64_t row1 = (row0 + L < T) ? row0 + L : T;
-    const int slab_rows = static_cast<int>(row1 - row0);  // <= L < 2^31
-    const int nsteps = (slab_rows + kStepRows - 1) / kStepRows;
+    const int tile = static_cast<int>(blockIdx.x) % tiles;
+    const int sg = static_cast<int>(blockIdx.x) / tiles;  // slab group, < G <= S
     const float kf = static_cast<float>(K);
     const int ki = static_cast<int>(K);  // K <= 2^22
     const uint32_t ready_addr = lds_addr(&ready[0]);
     const uint32_t consumed_addr = lds_addr(&consumed[0]);
-    // Rows of the slab from row 16 k on, clamped to one step.
+    const uint32_t poison_addr = lds_addr(&poison[0]);
+    // Rows of a slab from row 16 j on, clamped to one step.
     auto step_rows = [&](int rows_left) {
         return __builtin_amdgcn_readfirstlane(
             rows_left < 0 ? 0 : (rows_left > kStepRows ? kStepRows : rows_left));
     };
 
-    // ---- producer: raw P of step k into praw[k % kRawBufs], two 64-lane DMA
+    // ---- producer: raw P of a step into praw[k % kRawBufs], two 64-lane DMA
     // of 16 bytes for the 16 rows of grad_proj and, when dX is produced, one
     // of 4 bytes each for grad_r and r (the dW-only form is given neither).
     // Rows past the slab end read as zeros.
     const bool producer = wave == NW;
     constexpr int kRawDma = kDX ? 4 : 2;  // DMA instructions per step
-    auto issue_raw = [&](int k) {
-        const int rl = step_rows(slab_rows - kStepRows * k);
+    auto issue_raw = [&](int k, const StepCursor &at) {
+        const int rl = step_rows(at.slab_rows - kStepRows * at.j);
         RawStep &d = praw[k % kRawBufs];
-        const int64_t r0 = row0 + static_cast<int64_t>(kStepRows) * k;
+        const int64_t r0 = at.row0 + static_cast<int64_t>(kStepRows) * at.j;
         const __amdgpu_buffer_rsrc_t prs = make_rsrc32(grad_proj + r0 * kProjStride, rl * kProjStride * 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (MHCPB_LDS void *)(&d.p[0]), 16,
                                                  static_cast<uint32_t>(lane * 16), 0, 0, 0);
@@ -183,7 +243,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     };
 
     // The j = 24..31 entries of every operand slot are zero padding; the
-    // counters start at zero.
+    // counters and the poison word start at zero.
     constexpr int kPadJ = kJPad - kProjCols;
     for (int i = tid; i < kSlots * kStepRows * 2 * kPadJ; i += kThreads) {
         const int buf = i / (kStepRows * 2 * kPadJ);
@@ -201,23 +261,31 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         lds_write_u32(ready_addr + 4 * tid, 0u);
         lds_write_u32(consumed_addr + 4 * tid, 0u);
     }
+    if (tid == 0) lds_write_u32(poison_addr, 0u);
 
     if (producer) {
+        StepCursor ahead = cursor_start(sg, L, T);
 #pragma unroll
-        for (int k = 0; k < kRawAhead; ++k) issue_raw(k);
+        for (int k = 0; k < kRawAhead; ++k) {
+            issue_raw(k, ahead);
+            cursor_next(ahead, G, L, T);
+        }
         lds_barrier();
         // Lane = row * 4 + q converts j = 6q .. 6q + 5 of one row of P into
         // both operand layouts; lanes 0..15 also compute the RMS coefficient
         // grad_r / (r K) of row lane in FP32 (zero past the slab end).
         const int prow = lane / 4;
         const int pj0 = 6 * (lane % 4);
-        for (int k = 0; k < nsteps; ++k) {
-            issue_raw(k + kRawAhead);
+        StepCursor cur = cursor_start(sg, L, T);
+        for (int k = 0; cur.slab_rows > 0; ++k) {
+            issue_raw(k + kRawAhead, ahead);
+            cursor_next(ahead, G, L, T);
             // The raw P of step k was requested before that of the kRawAhead
             // steps after it, kRawDma DMA instructions each.
             wait_vmcnt<kRawDma * kRawAhead>();
             const int slot = k % kSlots;
-            lds_wait_at_least(consumed_addr + 4 * slot, NW * static_cast<uint32_t>(k / kSlots));
+            if (!lds_wait_at_least(consumed_addr + 4 * slot, NW * static_cast<uint32_t>(k / kSlots), max_polls))
+                lds_raise_poison(poison_addr, lane);
             const RawStep &src = praw[k % kRawBufs];
             const StepP &d = pop[slot];
             const uint32_t ra = lds_addr(&src.p[0]) + static_cast<uint32_t>((prow * kProjStride + pj0) * 4);
@@ -248,10 +316,11 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                 lds_write_u16_hi(pb1 + e * kPbJStride * 2, pk[e]);
             }
             if (kDX && lane < kStepRows) {
-                const bool in_slab = kStepRows * k + lane < slab_rows;
+                const bool in_slab = kStepRows * cur.j + lane < cur.slab_rows;
                 lds_write_u32(lds_addr(d.c + lane), __float_as_uint(in_slab ? grv / (rv * kf) : 0.f));
             }
             lds_signal(ready_addr + 4 * slot, lane);
+            cursor_next(cur, G, L, T);
         }
         // Drain the copies still in flight before the workgroup's LDS can be
         // released.
@@ -260,7 +329,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     }
 
     // ---- compute waves: X ring, W in registers.
-    const int64_t kw = static_cast<int64_t>(blockIdx.x) * (NW * 64) + wave * 64;
+    const int64_t kw = static_cast<int64_t>(tile) * (NW * 64) + wave * 64;
     const int kwi = static_cast<int>(kw);  // kw < K + NW * 64
     const int64_t col = kw + 4 * c16;      // first of this lane's 4 columns
     const bool active = col < K;
@@ -285,18 +354,26 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         const int n = rl * ki - kwi;
         return __builtin_amdgcn_readfirstlane(n > 0 ? n : 0);
     };
-    const int64_t row_bytes_x = K * 4;  // one row of X
     const int64_t row_bytes_d = K * 2;  // one row of dX or the addend
     const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&xring[wave][0][0][0]));
-    // xs points at row 0, column kw of a step; rows_left counts the slab rows
-    // from there on.
-    auto issue_x = [&](const char *xs, int rows_left, int stage) {
-        const __amdgpu_buffer_rsrc_t xrs = make_rsrc32(xs, range_elems(rows_left) * 4);
+    // The X request of the step `at` points to, into ring stage `stage`.
+    auto issue_x = [&](const StepCursor &at, int stage) {
+        const char *xs = reinterpret_cast<const char *>(x + (at.row0 + kStepRows * at.j) * K + kw);
+        const __amdgpu_buffer_rsrc_t xrs =
+            make_rsrc32(xs, range_elems(at.slab_rows - kStepRows * at.j) * 4);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xrs, (MHCPB_LDS void *)(&xring[wave][stage][rr][0]), 16, xoff[rr], 0, 0, MHCPB_X_AUX);
     };
+    // Partial dW stores: after the transpose through LDS (store_partial
+    // below) lane (c16, g) holds columns kw + 4 c16 .. + 3 of row j = 4 q + g
+    // for q = 0..5; a lane past K gets an offset outside the slab's range, so
+    // every partial write issues the same kPartialStores instructions.
+    uint32_t poff[kPartialStores];
+#pragma unroll
+    for (int q = 0; q < kPartialStores; ++q)
+        poff[q] = active ? static_cast<uint32_t>(((4 * q + g) * K + 4 * c16 + kw) * 4) : kOutOfRange;
     // W of this lane's columns (for the dX product): loaded first, then the X
     // of steps 0 and 1 (both ring stages are free at the start), so that the
     // wait for W below does not wait for X, and two steps stream in while the
@@ -314,10 +391,11 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
             }
     }
     compiler_fence();
-    const char *x_next = reinterpret_cast<const char *>(x + row0 * K + kw);
-    issue_x(x_next, slab_rows, 0);
-    issue_x(x_next + kStepRows * row_bytes_x, slab_rows - kStepRows, 1);
-    x_next += 2 * kStepRows * row_bytes_x;
+    StepCursor nxt = cursor_start(sg, L, T);  // the next step whose X is requested
+    issue_x(nxt, 0);
+    cursor_next(nxt, G, L, T);
+    issue_x(nxt, 1);
+    cursor_next(nxt, G, L, T);
     compiler_fence();
     // Padding and counters visible (the producer passes the same barrier).
     lds_barrier();
@@ -343,9 +421,50 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) accw[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Writes the partial dW of slab `slab_s` (or NaN when `poisoned`) to the
+    // workspace as whole 256-byte rows: the 32 x 64 block of accumulators
+    // (lane (c16, g), element e of block b: column kw + 16 g + 4 e + i of
+    // j = 16 b + c16) is transposed through `buf`, 4 KB of this wave's X ring
+    // that no request is writing, in two halves (rows 0..15, then 16..23), so
+    // that each store writes rows j = 4 q + g, columns kw + 4 c16 .. + 3.
+    // Whole lines need no fill in the L2; the stores use the default policy,
+    // so kernel 2 finds the slabs in the Infinity Cache.
+    auto store_partial = [&](int slab_s, uint32_t buf, bool poisoned) {
+        const __amdgpu_buffer_rsrc_t wrs =
+            make_rsrc32(ws + static_cast<int64_t>(slab_s) * kProjCols * K, kProjCols * ki * 4);
+        u32x4 tv[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (h == 0 || c16 < kProjCols - 16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    lds_write_u128(buf + static_cast<uint32_t>((c16 * 64 + 16 * g + 4 * e) * 4),
+                                   u32x4{__float_as_uint(accw[0][h][e]), __float_as_uint(accw[1][h][e]),
+                                         __float_as_uint(accw[2][h][e]), __float_as_uint(accw[3][h][e])});
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            constexpr int kQ = 4;
+            const int nq = h == 0 ? 4 : 2;
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+                if (q < nq) tv[q] = lds_read_u128(buf + static_cast<uint32_t>(((4 * q + g) * 64 + 4 * c16) * 4));
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(tv[0]), "+v"(tv[1]), "+v"(tv[2]), "+v"(tv[3])::"memory");
+            if (poisoned) {
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) tv[q] = u32x4{0x7FC00000u, 0x7FC00000u, 0x7FC00000u, 0x7FC00000u};
+            }
+            compiler_fence();
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+                if (q < nq) __builtin_amdgcn_raw_buffer_store_b128(tv[q], wrs, poff[4 * h + q], 0, 0);
+            compiler_fence();
+        }
+    };
 
-    char *d_cur = reinterpret_cast<char *>(dx + row0 * K + kw);
-    const char *a_cur = reinterpret_cast<const char *>(addend + row0 * K + kw);
+    StepCursor cur = cursor_start(sg, L, T);  // the step being computed
+    char *d_cur = reinterpret_cast<char *>(dx + cur.row0 * K + kw);
+    const char *a_cur = reinterpret_cast<const char *>(addend + cur.row0 * K + kw);
     // The ready count of a step's slot is read one step early, so that its
     // round trip is off the step's critical path.
     uint32_t ready_seen = lds_read_u32(ready_addr);
@@ -357,20 +476,26 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
     uint32_t pend[4][2] = {};
     char *d_prev = d_cur;
     int d_range_prev = 0;
-    for (int j = 0; j < nsteps; ++j) {
-        const int rows_left = slab_rows - kStepRows * j;
+    bool bad = false;           // this workgroup's results can no longer be trusted
+    bool after_unit = false;    // the previous step ended a unit (its partial was stored)
+    int last_unit_s = sg;       // slab of the unit whose partial is still to be stored
+    for (int k = 0; cur.slab_rows > 0; ++k) {
+        const int rows_left = cur.slab_rows - kStepRows * cur.j;
         // From the top of the step until the next X is requested the wave
         // runs at raised priority: once its X has arrived, the LDS reads and
         // the next request go ahead of the other waves' arithmetic on the
         // SIMD (about 1 % faster at T = 4096, K = 20480; the bits are those
         // of the same kernel without it).
         __builtin_amdgcn_s_setprio(1);
-        const int slot = j % kSlots;
+        const int slot = k % kSlots;
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ready_seen)::"memory");
-        const uint32_t want = static_cast<uint32_t>(j / kSlots + 1);
-        if (__builtin_amdgcn_readfirstlane(ready_seen) < want)
-            lds_wait_at_least(ready_addr + 4 * slot, want);
-        const StepP &cur = pop[slot];
+        const uint32_t want = static_cast<uint32_t>(k / kSlots + 1);
+        if (__builtin_amdgcn_readfirstlane(ready_seen) < want &&
+            !lds_wait_at_least(ready_addr + 4 * slot, want, max_polls)) {
+            bad = true;
+            lds_raise_poison(poison_addr, lane);
+        }
+        const StepP &cur_p = pop[slot];
         // The P operands of this step are requested first: the RMS
         // coefficients of rows 4g..4g+3, the dX P operands (token c16, part
         // p, j = 16b + 4g .. +3) and the dW P operands (part p, j = 16b +
@@ -378,56 +503,70 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
         f32x4 cc = {};
         u32x4 pa[2][2] = {};  // [part][block]
         u32x4 pbv[2] = {};    // [block]: part 0 in .xy, part 1 in .zw
-        if constexpr (kDX) cc = lds_read_b128(lds_addr(cur.c + 4 * g));
+        if constexpr (kDX) cc = lds_read_b128(lds_addr(cur_p.c + 4 * g));
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             if constexpr (kDX) {
 #pragma unroll
                 for (int p = 0; p < 2; ++p)
                     pa[p][b] = lds_read_u128(
-                        lds_addr(cur.pa + c16 * kPaStride + p * kJPad + 16 * b + 4 * g));
+                        lds_addr(cur_p.pa + c16 * kPaStride + p * kJPad + 16 * b + 4 * g));
             }
             if constexpr (kDW)
-                pbv[b] = lds_read_u128(lds_addr(cur.pb + (16 * b + c16) * kPbJStride + 8 * g));
+                pbv[b] = lds_read_u128(lds_addr(cur_p.pb + (16 * b + c16) * kPbJStride + 8 * g));
         }
-        // Then wait for this step's X and read it (4 rows).  Step j >= 1
-        // issues, in this order: [4 addend loads] 4 X DMA (for step j + 1),
-        // [4 dX stores of step j - 1 when deferred], [4 dX stores of step j
-        // otherwise]; step 0 issues no X (the prologue requested steps 0 and
-        // 1, after the W loads).  So after the X of step j come at most 4
-        // stores (of step j - 1, or of step j - 2 when deferred; none without
-        // dX), and after the X of step 0 the X of step 1: vmcnt(4), or
-        // vmcnt(0) for the later steps of the dW-only form, covers it.  With
-        // deferred stores step 0 stores nothing, so step 1 waits for
-        // vmcnt(0).  For step 1 with the addend, step 0's addend loads come
-        // after the X of step 1 as well, and the wait is only stricter.
-        // Steps past the slab end are still requested (they read zeros;
-        // their stores fall outside the range), which keeps every step's
-        // count identical.
-        if (j == 0 || (kDX && !(kDefer && j == 1)))
-            wait_vmcnt<4>();
-        else
-            wait_vmcnt<0>();
-        const uint32_t xa = ring_base + static_cast<uint32_t>((((j & 1) * 4) * kWave + lane) * 16);
+        // Then wait for this step's X and read it (4 rows).  Step k >= 1
+        // issues, in this order: [4 addend loads] 4 X DMA (for step k + 1),
+        // [4 dX stores of step k - 1 when deferred], [4 dX stores of step k
+        // otherwise], [the kPartialStores partial stores when step k ends a
+        // unit]; step 0 issues no X (the prologue requested steps 0 and 1,
+        // after the W loads).  So after the X of step k come at most 4 dX
+        // stores (of step k - 1, or of step k - 2 when deferred; none without
+        // dX) and, when step k - 1 ended a unit, that unit's partial stores;
+        // after the X of step 0 the X of step 1: vmcnt(4), or vmcnt(0) for
+        // the later steps of the dW-only form, plus kPartialStores after a
+        // unit's end, covers it.  With deferred stores step 0 stores nothing,
+        // so step 1 waits for vmcnt(0) (or the partial stores alone).  For
+        // step 1 with the addend, step 0's addend loads come after the X of
+        // step 1 as well, and the wait is only stricter.  Steps past the slab
+        // end are still requested (they read zeros; their stores fall outside
+        // the range), which keeps every step's count identical.
+        const bool four = k == 0 || (kDX && !(kDefer && k == 1));
+        if (!after_unit || !kDW) {
+            if (four)
+                wait_vmcnt<4>();
+            else
+                wait_vmcnt<0>();
+        } else {
+            if (four)
+                wait_vmcnt<4 + kPartialStores>();
+            else
+                wait_vmcnt<kPartialStores>();
+        }
+        const uint32_t xa = ring_base + static_cast<uint32_t>((((k & 1) * 4) * kWave + lane) * 16);
         f32x4 xc[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) xc[rr] = lds_read_b128(xa + rr * kWave * 16);
+        // The poison word is read after the slot: a producer that gave up
+        // raised it before it overwrote a slot.
+        uint32_t pois = lds_read_u32(poison_addr);
         // The wait names every register the reads above return, so no use
         // of them can be scheduled before the data has arrived.
         if constexpr (kDX && kDW)
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
                            "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]), "+v"(pa[1][1]),
-                           "+v"(pbv[0]), "+v"(pbv[1])::"memory");
+                           "+v"(pbv[0]), "+v"(pbv[1]), "+v"(pois)::"memory");
         else if constexpr (kDX)
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
                            "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]),
-                           "+v"(pa[1][1])::"memory");
+                           "+v"(pa[1][1]), "+v"(pois)::"memory");
         else
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(pbv[0]),
-                           "+v"(pbv[1])::"memory");
+                           "+v"(pbv[1]), "+v"(pois)::"memory");
+        bad = bad || __builtin_amdgcn_readfirstlane(pois) != 0;
         lds_signal(consumed_addr + 4 * slot, lane);
         uint2 av[4] = {};
         const int d_range = range_elems(rows_left) * 2;
@@ -438,16 +577,15 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                 const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ars, doff[rr], 0, 0);
                 av[rr] = make_uint2(v.x, v.y);
             }
-            a_cur += kStepRows * row_bytes_d;
         }
         compiler_fence();
-        if (j > 0) {
-            issue_x(x_next, rows_left - kStepRows, (j + 1) & 1);
-            x_next += kStepRows * row_bytes_x;
+        if (k > 0) {
+            issue_x(nxt, (k + 1) & 1);
+            cursor_next(nxt, G, L, T);
         }
         compiler_fence();
         __builtin_amdgcn_s_setprio(0);
-        if (kDefer && j > 0) {
+        if (kDefer && k > 0) {
             const __amdgpu_buffer_rsrc_t prs =
                 make_rsrc32(uniform_ptr(d_prev), __builtin_amdgcn_readfirstlane(d_range_prev));
 #pragma unroll
@@ -509,6 +647,10 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                     packed[rr][i >> 1] = __float_as_uint(d);
             }
         }
+        if (bad) {  // results past a give-up are not trusted: two BF16 NaNs per word
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) packed[rr][0] = packed[rr][1] = 0x7FC07FC0u;
+        }
         // One rounding to BF16 per element (above), then 8-byte range-checked
         // stores: rows past the slab end are dropped.
         if constexpr (kDefer) {
@@ -527,9 +669,32 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                                                       doff[rr], 0, MHCPB_DX_AUX);
         }
         d_cur += kStepRows * row_bytes_d;
-        ready_seen = lds_read_u32(ready_addr + 4 * ((j + 1) % kSlots));
+        if constexpr (kAddend) a_cur += kStepRows * row_bytes_d;
+        ready_seen = lds_read_u32(ready_addr + 4 * ((k + 1) % kSlots));
+        const int s_done = sg + cur.u * G;
+        after_unit = cursor_next(cur, G, L, T);
+        if (after_unit) {
+            d_cur = reinterpret_cast<char *>(dx + cur.row0 * K + kw);
+            if constexpr (kAddend) a_cur = reinterpret_cast<const char *>(addend + cur.row0 * K + kw);
+        }
+        // At the end of a unit that is not the last, its partial dW goes to
+        // workspace slab s_done while the X of the next unit is already in
+        // flight (through ring stage k & 1, which holds no request until the
+        // next step); the accumulators restart from zero.  The last unit's
+        // partial is stored after the drain below.
+        if (kDW && after_unit) {
+            if (cur.slab_rows > 0) {
+                store_partial(s_done, ring_base + static_cast<uint32_t>((k & 1) * 4 * kWave * 16), bad);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int jb = 0; jb < 2; ++jb) accw[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                last_unit_s = s_done;
+            }
+        }
     }
-    if (kDefer && nsteps > 0) {  // the last step's stores
+    if constexpr (kDefer) {  // the last step's stores
         const __amdgpu_buffer_rsrc_t prs =
             make_rsrc32(uniform_ptr(d_prev), __builtin_amdgcn_readfirstlane(d_range_prev));
 #pragma unroll
@@ -538,95 +703,99 @@ __attribute__((amdgpu_waves_per_eu(3))) void projection_kernel(
                                                   0, MHCPB_DX_AUX);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ready_seen)::"memory");
-    // Drain the X DMA still in flight (the step past the slab end) before
+    // Drain the X DMA still in flight (the steps past the last unit) before
     // the workgroup's LDS can be released.
     wait_vmcnt<0>();
 
-    // Partial dW of this slab, written once to workspace slab s.  Lane
-    // (c16, g), element e of block jb holds column kw + 16 g + 4 e + i of
-    // j = 16 jb + c16.  The wave's 32 x 64 block goes through its own X ring
-    // (8 KB, idle after the drain above) so that each store instruction
-    // writes four whole 256-byte rows: j = 4 q + g, columns kw + 4 c16 ..
-    // + 3.  With whole lines the stores can be non-temporal (with the
-    // 64-byte pieces of the register layout they cost about 10 us more).
-    if constexpr (!kDW) return;
-    float *slab = ws + static_cast<int64_t>(s) * kProjCols * K;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            lds_write_u128(ring_base + static_cast<uint32_t>(((16 * b + c16) * 64 + 16 * g + 4 * e) * 4),
-                           u32x4{__float_as_uint(accw[0][b][e]), __float_as_uint(accw[1][b][e]),
-                                 __float_as_uint(accw[2][b][e]), __float_as_uint(accw[3][b][e])});
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    static_assert(kProjCols / 4 == 6, "the wait below names the six rows of four");
-    u32x4 tv[kProjCols / 4];
-#pragma unroll
-    for (int q = 0; q < kProjCols / 4; ++q)
-        tv[q] = lds_read_u128(ring_base + static_cast<uint32_t>(((4 * q + g) * 64 + 4 * c16) * 4));
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(tv[0]), "+v"(tv[1]), "+v"(tv[2]), "+v"(tv[3]), "+v"(tv[4]), "+v"(tv[5])::"memory");
-    if (active) {
-#pragma unroll
-        for (int q = 0; q < kProjCols / 4; ++q)
-            __builtin_nontemporal_store(__builtin_bit_cast(f32x4, tv[q]),
-                                        reinterpret_cast<f32x4 *>(slab + (4 * q + g) * K + col));
-    }
+    // Partial dW of the last unit, written once to workspace slab
+    // last_unit_s (the ring is idle after the drain).
+    if constexpr (kDW) store_partial(last_unit_s, ring_base, bad);
 }
 
-// dW[i] = (((ws[0][i] + ws[1][i]) + ws[2][i]) + ...), four elements per thread.
-// The slabs are loaded eight at a time before they are added (in order), so
-// the loads overlap.
+// dW[i] = (((ws[0][i] + ws[1][i]) + ws[2][i]) + ...), four elements (one
+// quad) per column group; a thread takes kReduceQuads quads spaced by the
+// grid's thread count, and requests eight slabs of each of them before it
+// adds them in order, so that 8 x kReduceQuads loads are in flight.
+#ifndef MHCPB_K2_QPT
+#define MHCPB_K2_QPT 1
+#endif
 constexpr int kReduceBatch = 8;
+constexpr int kReduceQuads = MHCPB_K2_QPT;
 __global__ __launch_bounds__(256) void reduce_slabs(const float *__restrict__ ws,
                                                     float *__restrict__ dw, int S,
                                                     int64_t n4) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= n4) return;
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(ws) + i;
-    f32x4 a = __builtin_nontemporal_load(src);
+    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(ws);
+    f32x4 a[kReduceQuads];
+#pragma unroll
+    for (int q = 0; q < kReduceQuads; ++q) {
+        const int64_t i = i0 + q * nthreads;
+        a[q] = i < n4 ? __builtin_nontemporal_load(src + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
-        f32x4 b[kReduceBatch];
+        f32x4 b[kReduceQuads][kReduceBatch];
         // Past the last slab the addend is -0, which leaves every sum as it
         // is (x + -0 == x, signed zeros included).
 #pragma unroll
-        for (int u = 0; u < kReduceBatch; ++u)
-            b[u] = (s0 + u < S) ? __builtin_nontemporal_load(src + static_cast<int64_t>(s0 + u) * n4)
-                                : f32x4{-0.f, -0.f, -0.f, -0.f};
+        for (int q = 0; q < kReduceQuads; ++q)
 #pragma unroll
-        for (int u = 0; u < kReduceBatch; ++u) a += b[u];
+            for (int u = 0; u < kReduceBatch; ++u) {
+                const int64_t i = i0 + q * nthreads;
+                b[q][u] = (s0 + u < S && i < n4)
+                              ? __builtin_nontemporal_load(src + static_cast<int64_t>(s0 + u) * n4 + i)
+                              : f32x4{-0.f, -0.f, -0.f, -0.f};
+            }
+#pragma unroll
+        for (int q = 0; q < kReduceQuads; ++q)
+#pragma unroll
+            for (int u = 0; u < kReduceBatch; ++u) a[q] += b[q][u];
     }
-    reinterpret_cast<f32x4 *>(dw)[i] = a;
+#pragma unroll
+    for (int q = 0; q < kReduceQuads; ++q) {
+        const int64_t i = i0 + q * nthreads;
+        if (i < n4) reinterpret_cast<f32x4 *>(dw)[i] = a[q];
+    }
+}
+
+// Slab groups G of kernel 1: enough workgroups (tiles x G) for one per CU of
+// a 256-CU GPU where the tiles allow it, never more groups than slabs.  A
+// performance choice only: no bit of the result depends on it.
+constexpr int kTargetWorkgroups = 256;
+inline int slab_groups(int tiles, int S) {
+    int G = kTargetWorkgroups / (tiles > 0 ? tiles : 1);
+    if (G > S) G = S;
+    return G < 1 ? 1 : G;
 }
 
 template <int NW>
 hipError_t launch_projection_t(const Plan &p, const Args &a, Outputs out, hipStream_t stream,
                                hipEvent_t start, hipEvent_t stop) {
     constexpr int cols = NW * 64;
-    const dim3 grid(static_cast<unsigned>((p.K + cols - 1) / cols), static_cast<unsigned>(p.S));
+    const int tiles = static_cast<int>((p.K + cols - 1) / cols);
+    const int G = slab_groups(tiles, p.S);
+    const dim3 grid(static_cast<unsigned>(tiles) * static_cast<unsigned>(G));
     const dim3 block((NW + 1) * kWave);
 #define MHCPB_LAUNCH(ADD, DX, DW)                                                               \
-    launch(projection_kernel<NW, ADD, DX, DW>, grid, block, stream, start, stop, a.x, a.w,      \
-           a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L)
+    return launch(projection_kernel<NW, ADD, DX, DW>, grid, block, stream, start, stop, a.x, a.w, \
+           a.grad_proj, a.grad_r, a.r, a.dx, a.ws, a.addend, p.T, p.K, p.L, p.S, tiles, G,     \
+           p.wait_polls)
     switch (out) {
     case Outputs::kBoth:
         if (a.addend)
             MHCPB_LAUNCH(true, true, true);
         else
             MHCPB_LAUNCH(false, true, true);
-        break;
     case Outputs::kDxOnly:
         if (a.addend)
             MHCPB_LAUNCH(true, true, false);
         else
             MHCPB_LAUNCH(false, true, false);
-        break;
     case Outputs::kDwOnly:
         MHCPB_LAUNCH(false, false, true);
-        break;
     }
 #undef MHCPB_LAUNCH
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -643,9 +812,8 @@ hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStrea
 
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop) {
     const int64_t n4 = kProjCols * p.K / 4;
-    const unsigned blocks = static_cast<unsigned>((n4 + 255) / 256);
-    launch(reduce_slabs, dim3(blocks), dim3(256), stream, nullptr, stop, a.ws, a.dw, p.S, n4);
-    return hipGetLastError();
+    const unsigned blocks = static_cast<unsigned>((n4 + 256 * kReduceQuads - 1) / (256 * kReduceQuads));
+    return launch(reduce_slabs, dim3(blocks), dim3(256), stream, nullptr, stop, a.ws, a.dw, p.S, n4);
 }
 
 }  // namespace mhcpb

@@ -9,6 +9,7 @@
 // entry points (the map the stage differentiates) use the same plan.
 #include <algorithm>
 #include <cstdint>
+#include <cstdlib>
 #include <new>
 
 #include "../../include/mhcpb.h"
@@ -188,6 +189,20 @@ mhcpb_status_t run_rmsnorm(int64_t T, int32_t H, const uint16_t *g, const uint16
     return MHCPB_SUCCESS;
 }
 
+// The bound of the kernels' LDS counter waits for a new plan: the default,
+// or the value of the environment variable when it holds a decimal integer in
+// [0, 2^20] (anything else is ignored).
+int32_t wait_polls_setting() {
+    const char *v = std::getenv(mhcpb::kWaitPollsEnv);
+    if (!v || !*v)
+        return mhcpb::kDefaultWaitPolls;
+    char *end = nullptr;
+    const long n = std::strtol(v, &end, 10);
+    if (*end != '\0' || n < 0 || n > (1L << 20))
+        return mhcpb::kDefaultWaitPolls;
+    return static_cast<int32_t>(n);
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,6 +224,7 @@ mhcpb_status_t mhcpb_plan_create(mhcpb_plan_t *plan, int64_t T, int32_t streams,
     p.S = mhcpb::split_count(T);
     p.L = (T + p.S - 1) / p.S;
     p.ws_bytes = static_cast<size_t>(p.S) * mhcpb::kProjCols * static_cast<size_t>(p.K) * 4;
+    p.wait_polls = wait_polls_setting();
     auto *h = new (std::nothrow) mhcpb_plan_s{p};
     if (!h)
         return MHCPB_ERROR_INVALID_ARGUMENT;

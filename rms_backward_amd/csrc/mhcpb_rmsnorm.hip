@@ -353,8 +353,8 @@ hipError_t launch_rmsnorm_backward(const RmsPlan &p, const uint16_t *g, const ui
         RowsKernel k = rows_kernel(nc, w_f32, res != nullptr, in_bytes >= kRmsStreamBytes);
         if (!k) return hipErrorInvalidValue;
         RmsArgs a{g, x, w, rstd, res, dx, ws, p.T, p.H};
-        launch(k, dim3(static_cast<unsigned>(p.S)), dim3(nc * kWave), stream, start, mid, a);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch(k, dim3(static_cast<unsigned>(p.S)), dim3(nc * kWave), stream,
+                                    start, mid, a);
         if (e != hipSuccess) return e;
     }
     else if (start || mid) {
@@ -363,9 +363,8 @@ hipError_t launch_rmsnorm_backward(const RmsPlan &p, const uint16_t *g, const ui
         if (mid && hipEventRecord(mid, stream) != hipSuccess) return hipErrorLaunchFailure;
     }
     const unsigned blocks = static_cast<unsigned>((p.H + kWave - 1) / kWave);
-    launch(rmsnorm_dw_reduce, dim3(blocks), dim3(kReduceGroups * kWave), stream, nullptr, stop,
-           static_cast<const float *>(ws), dw, static_cast<int>(p.S), p.H);
-    return hipGetLastError();
+    return launch(rmsnorm_dw_reduce, dim3(blocks), dim3(kReduceGroups * kWave), stream, nullptr,
+                  stop, static_cast<const float *>(ws), dw, static_cast<int>(p.S), p.H);
 }
 
 }  // namespace mhcpb
