@@ -173,19 +173,6 @@ int oracle_dw(int mode, int64_t rows, int64_t cols,
     return 0;
 }
 
-/* Both outputs over the whole [T, K] problem. */
-int oracle_mhcpb_backward(int mode, int64_t T, int64_t K,
-                          const float *x, const float *w,
-                          const float *grad_proj, const float *grad_r,
-                          const float *r, const uint16_t *addend,
-                          double *dx, double *dw)
-{
-    int rc = oracle_dx(mode, T, K, K, x, w, grad_proj, grad_r, r, addend, dx);
-    if (rc != 0)
-        return rc;
-    return oracle_dw(mode, T, K, x, grad_proj, dw);
-}
-
 /*
  * The forward map of the stage: the 24 gate logits and the RMS of each row,
  * in one pass over X.

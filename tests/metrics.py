@@ -47,6 +47,21 @@ def bf16_bits_to_f64(bits):
     return b.view(np.float32).astype(np.float64)
 
 
+TINY = 2.0 ** -126  # the smallest normal FP32 (and BF16) number
+
+
+def flush_bound(abs_a, abs_b, n_products):
+    """Bound of what the matrix-unit products may lose against the oracle
+    below the normal range (a known departure): the BF16 matrix units read
+    subnormal inputs as zero, so a TF32 operand split into BF16 high and low
+    parts loses any part below 2^-126, and a partial product or partial sum
+    below 2^-126 may be lost as well.  Per product a * b that is at most
+    2^-126 (|a| + |b| + 5); abs_a and abs_b bound |a| and |b| summed over the
+    products (or elementwise, with n_products the product count)."""
+    return TINY * (np.asarray(abs_a, dtype=np.float64) + np.asarray(abs_b, dtype=np.float64)
+                   + 5.0 * n_products)
+
+
 def dw_accumulation_bound(abs_sum, rows_per_slab, splits):
     """Worst-case FP32 summation error of the slab-then-fixed-order scheme:
     at most (rows_per_slab + splits + 64) roundings of 2^-24, each bounded by
