@@ -134,6 +134,26 @@ mhcpb_status_t mhcpb_execute_with_events(
     hipEvent_t after_k2);
 
 /*
+ * mhcpb_execute without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The partial dW slabs go to a static workspace of
+ * 64 MiB (67,108,864 bytes) per GPU that the library holds from its load
+ * until the process ends; the call allocates nothing.  Arguments, results and
+ * errors are those of mhcpb_execute, plus MHCPB_ERROR_WORKSPACE when the
+ * plan's workspace (mhcpb_workspace_bytes) exceeds 64 MiB (T > 16384 at
+ * K = 20480) and MHCPB_ERROR_LAUNCH when the static workspace cannot be
+ * located on the current device.  The device is the calling thread's current
+ * one (hipGetDevice), which must be the device of `stream` and the buffers.
+ * Every such call on one GPU shares that workspace: calls that overlap in
+ * time on one GPU (other streams, other threads) race and may give wrong
+ * results; serialise them or use mhcpb_execute with separate workspaces.
+ */
+mhcpb_status_t mhcpb_execute_noalloc(mhcpb_plan_t plan, const float *x, const float *w,
+                                     const float *grad_proj, const float *grad_r,
+                                     const float *r, uint16_t *dx, float *dw,
+                                     const uint16_t *grad_x_addend, hipStream_t stream);
+
+/*
  * The split backward ("FP8 weight cache, split backward, fused mHC stream
  * gradient" on the prime-kernels page: dX is produced by its own call, so
  * that it can be handed on while dW is still to be computed).  Each

@@ -39,7 +39,7 @@ MHCPB_ERROR_LAUNCH = 6
 EXPORTED = (
     "mhcpb_plan_create", "mhcpb_plan_destroy", "mhcpb_workspace_bytes",
     "mhcpb_plan_split_count", "mhcpb_execute", "mhcpb_execute_with_events",
-    "mhcpb_execute_dx", "mhcpb_execute_dw", "mhcpb_status_string",
+    "mhcpb_execute_noalloc", "mhcpb_execute_dx", "mhcpb_execute_dw", "mhcpb_status_string",
     "mhcpb_forward_workspace_bytes", "mhcpb_forward", "mhcpb_forward_with_events",
     "mhcpb_rmsnorm_backward_workspace_bytes", "mhcpb_rmsnorm_backward",
     "mhcpb_rmsnorm_backward_with_events",
@@ -63,6 +63,8 @@ _lib.mhcpb_execute.argtypes = _EXEC_ARGS
 _lib.mhcpb_execute.restype = ctypes.c_int
 _lib.mhcpb_execute_with_events.argtypes = _EXEC_ARGS + [_vp, _vp, _vp]
 _lib.mhcpb_execute_with_events.restype = ctypes.c_int
+_lib.mhcpb_execute_noalloc.argtypes = [_vp] * 10
+_lib.mhcpb_execute_noalloc.restype = ctypes.c_int
 _lib.mhcpb_execute_dx.argtypes = [_vp] * 8 + [_vp]
 _lib.mhcpb_execute_dx.restype = ctypes.c_int
 _lib.mhcpb_execute_dw.argtypes = [_vp] * 5 + [ctypes.c_size_t, _vp]
@@ -167,6 +169,18 @@ def mhcpb_execute_with_events(plan, x, w, grad_proj, grad_r, r, dx, dw, grad_x_a
         before_k1, after_k1, after_k2)
     if check and st != MHCPB_SUCCESS:
         raise MhcpbError(st, "mhcpb_execute_with_events")
+    return st
+
+
+def mhcpb_execute_noalloc(plan, x, w, grad_proj, grad_r, r, dx, dw, grad_x_addend,
+                          stream: int = 0, check: bool = True) -> int:
+    """mhcpb_execute with the library's static per-GPU workspace (64 MiB) in
+    place of a caller workspace: allocates nothing.  Calls that overlap on one
+    GPU race on that workspace."""
+    st = _lib.mhcpb_execute_noalloc(plan, _ptr(x), _ptr(w), _ptr(grad_proj), _ptr(grad_r),
+                                    _ptr(r), _ptr(dx), _ptr(dw), _ptr(grad_x_addend), stream)
+    if check and st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_execute_noalloc")
     return st
 
 

@@ -72,6 +72,12 @@ hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStrea
 // takes the end time of the dispatch.
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop);
 
+// The static workspace of mhcpb_execute_noalloc: kStaticWorkspaceBytes of
+// device memory per GPU in a file-scope array of the kernel library.
+// static_workspace() gives its address on the current device (looked up once
+// per device, then cached); it allocates nothing.
+constexpr size_t kStaticWorkspaceBytes = size_t{64} << 20;
+hipError_t static_workspace(void **ptr);
 
 // Forward: the K columns are cut into tiles of kFwdTileCols; kernel 1
 // writes one partial (24 logits and a sum of squares) per tile and token into

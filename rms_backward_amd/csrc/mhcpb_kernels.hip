@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "mhcpb_device.h"
 #include "mhcpb_internal.h"
@@ -814,6 +815,34 @@ hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEv
     const int64_t n4 = kProjCols * p.K / 4;
     const unsigned blocks = static_cast<unsigned>((n4 + 256 * kReduceQuads - 1) / (256 * kReduceQuads));
     return launch(reduce_slabs, dim3(blocks), dim3(256), stream, nullptr, stop, a.ws, a.dw, p.S, n4);
+}
+
+// Static workspace for callers that cannot allocate (mhcpb_execute_noalloc).
+// One copy per GPU, held from the library's load until the process ends; the
+// kernels take the address hipGetSymbolAddress gives for the current device,
+// never the host-side name of the array.
+namespace {
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_workspace(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace mhcpb

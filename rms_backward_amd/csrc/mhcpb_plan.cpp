@@ -270,6 +270,21 @@ mhcpb_status_t mhcpb_execute_with_events(mhcpb_plan_t plan, const float *x, cons
                workspace, workspace_size, stream, before_k1, after_k1, after_k2);
 }
 
+mhcpb_status_t mhcpb_execute_noalloc(mhcpb_plan_t plan, const float *x, const float *w,
+                                     const float *grad_proj, const float *grad_r, const float *r,
+                                     uint16_t *dx, float *dw, const uint16_t *grad_x_addend,
+                                     hipStream_t stream) {
+    if (!plan)
+        return MHCPB_ERROR_INVALID_ARGUMENT;
+    if (plan->plan.ws_bytes > mhcpb::kStaticWorkspaceBytes)
+        return MHCPB_ERROR_WORKSPACE;
+    void *ws = nullptr;
+    if (mhcpb::static_workspace(&ws) != hipSuccess)
+        return MHCPB_ERROR_LAUNCH;
+    return run(plan, mhcpb::Outputs::kBoth, x, w, grad_proj, grad_r, r, dx, dw, grad_x_addend, ws,
+               mhcpb::kStaticWorkspaceBytes, stream, nullptr, nullptr, nullptr);
+}
+
 mhcpb_status_t mhcpb_execute_dx(mhcpb_plan_t plan, const float *x, const float *w,
                                 const float *grad_proj, const float *grad_r, const float *r,
                                 uint16_t *dx, const uint16_t *grad_x_addend,
