@@ -6,9 +6,23 @@
 One step is one call of mhcpb_execute (kernel 1 + kernel 2) on the synthetic
 workload, with every input already resident in HBM.  Prints ONE JSON line:
 microseconds per call, achieved GB/s of algorithmic bytes (value), the
-roofline of the dominant kernel (kernel 1, timed per launch with HIP events
-recorded by the library on the launch stream) and the CPU oracle timed on a
-bounded sample of the same workload.
+roofline of the dominant kernel (kernel 1) and the CPU oracle timed on a
+bounded sample of the same workload over the host's cores.
+
+Timing.  The library's code object is loaded first (one call on a 16-token
+problem).  Before the warm-up the GPU then runs about 300 ms of BF16 matrix
+products on scratch matrices (torch, none of the library's kernels, inputs or
+outputs): after an idle spell the GPU's power management slows calls 10 to
+150 by up to 35 % (measured on the box: a transient after idle, gone after a
+few tens of milliseconds of compute-heavy work, such as the GEMMs that
+surround this stage in a training step), and the settle takes the device out
+of it without running extra steps of the path.  Then W warm-up calls and
+exactly K timed calls back to back on one stream, bracketed by events.  The
+roofline's kernel-1 duration comes from an event pass right after the timed
+calls (at least 100 more calls, each with HIP events the library attaches to
+its two dispatches): attaching events to a call costs about 4 us per call
+(measured), so the timed calls run without them; the fraction is reported
+only if kernel 1 and kernel 2 of that pass fit in the timed time per call.
 
 Algorithmic bytes per call (T tokens, K columns, S splits):
     X T*K*4 + dX T*K*2 [+ addend T*K*2] + W 24*K*4 + P 24*T*4 + grad_r, r 2*T*4
@@ -32,6 +46,8 @@ METRIC = "µs/call and achieved HBM GB/s (% of peak) at T=4096, K=4×5120"
 KERNEL_SOURCES = [os.path.join(ROOT, "rms_backward_amd", "csrc", n)
                   for n in ("mhcpb_kernels.hip", "mhcpb_device.h")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "projection_train_counters.json")
+TRACE_FILE = os.path.join(ROOT, "profiles", "projection_train_kernel_stats.json")
+SETTLE_MS = 300.0
 
 
 def algorithmic_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
@@ -44,12 +60,11 @@ def algorithmic_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
     return call, k1
 
 
-def kernel_source_hash() -> str:
-    """Hash of the backward kernels' source (the kernel file and the device
-    helpers it includes) with comments, blank lines and trailing spaces
+def source_hash(paths) -> str:
+    """Hash of kernel sources with comments, blank lines and trailing spaces
     removed: it changes with the code, not with its comments."""
     text = ""
-    for path in KERNEL_SOURCES:
+    for path in paths:
         with open(path, encoding="utf-8") as f:
             text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -58,19 +73,35 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per kernel-1 launch from the committed counter summary, if it
-    was taken on the current kernel source; otherwise None."""
+def kernel_source_hash() -> str:
+    return source_hash(KERNEL_SOURCES)
+
+
+def _profile_record(path: str, workload: str, sha: str):
+    """A committed profile summary (JSON) taken on the current kernel source
+    and workload, else None."""
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != sha or rec.get("workload") != workload:
         return None
-    if rec.get("workload") != workload:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per kernel-1 launch from the committed counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    rec = _profile_record(COUNTERS_FILE, workload, kernel_source_hash())
+    return rec.get("hbm_bytes_per_launch") if rec else None
+
+
+def profiled_kernel1_us(workload: str):
+    """Kernel 1's average duration in the committed rocprofv3 kernel trace of
+    the current source, in microseconds, if there is one; otherwise None."""
+    rec = _profile_record(TRACE_FILE, workload, kernel_source_hash())
+    return rec.get("kernel1_avg_us") if rec else None
 
 
 class HipEvents:
@@ -100,32 +131,177 @@ class HipEvents:
         self.lib.hipEventDestroy(h)
 
 
-def cpu_baseline(inp, rows: int, T: int, K: int, S: int, addend: bool):
-    """Time the FP64 oracle (as it is, one thread) on the first `rows` rows."""
-    import numpy as np
+def device_settle(ms: float) -> dict:
+    """About `ms` milliseconds of BF16 matrix products on scratch matrices
+    (none of the library's kernels, inputs or outputs), so that the timed
+    calls do not start inside the GPU's power-management transient after
+    idle (fills of memory alone leave about a third of it)."""
+    import torch
+    if ms <= 0:
+        return {"ms": 0}
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    c = a @ a  # the GEMM library's own start-up, outside the settle time
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < ms / 1e3:
+        c = a @ a
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) * 1e3
+    del a, c
+    return {"ms": round(dt, 1), "bf16_gemms_8192": n}
 
+
+def load_kernels(stage: str):
+    """One call of the stage's entry point on a 16-token problem, so that the
+    runtime loads the library's code object on the GPU before the settle (the
+    load happens at a module's first launch and takes tens of milliseconds,
+    long enough for the GPU to leave the state the settle put it in)."""
+    import torch
+    import workloads
+    from tests import gpu_harness as gh
+    if stage == "rmsnorm":
+        gh.run_rmsnorm(workloads.rms_inputs(workloads.rms_custom(16, 64), "cuda"))
+    elif stage == "forward":
+        inp = workloads.forward_inputs(workloads.custom(16, 4, 16), "cuda")
+        gh.run_forward(inp["x"], inp["w"])
+    else:
+        gh.run(workloads.make(workloads.custom(16, 4, 16), "cuda"))
+    torch.cuda.synchronize()
+
+
+def timed_calls(call, steps: int):
+    """Exactly `steps` calls back to back on the current stream, bracketed by
+    torch events; returns (µs per call, wall seconds)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps, time.perf_counter() - t0
+
+
+def event_pass(call_with_events, calls: int):
+    """`calls` calls, each with three HIP events attached to its dispatches by
+    the library (kernel 1 start, kernel 1 end, kernel 2 end); returns the
+    kernel-1 and kernel-2 (with the gap before it) durations in µs."""
+    import torch
+    hev = HipEvents()
+    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(calls)]
+    torch.cuda.synchronize()
+    for a, b, c in evs:
+        call_with_events(a, b, c)
+    torch.cuda.synchronize()
+    k1 = [hev.elapsed_ms(a, b) * 1e3 for a, b, _ in evs]
+    k2 = [hev.elapsed_ms(b, c) * 1e3 for _, b, c in evs]
+    for trio in evs:
+        for e in trio:
+            hev.destroy(e)
+    return k1, k2
+
+
+def _median(v):
+    s = sorted(v)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def roofline(kernel: str, bytes_per_launch: int, k1: list, k2: list, us_per_call: float,
+             traffic, profile_us) -> dict:
+    """Roofline object of kernel 1 from its durations in the event pass.  A
+    fraction is only reported when kernel 1 and kernel 2 fit in the timed
+    time per call (durations that do not fit are not evidence)."""
+    k1_mean = sum(k1) / len(k1)
+    k2_mean = sum(k2) / len(k2)
+    consistent = k1_mean + k2_mean <= us_per_call * 1.02
+    achieved = bytes_per_launch / (k1_mean * 1e-6) / 1e9
+    out = {
+        "bound": "hbm",
+        "achieved": round(achieved, 2) if consistent else None,
+        "peak": PEAK_HBM_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_HBM_GBPS, 4) if consistent else None,
+        "traffic": traffic,
+        "kernel": kernel,
+        "bytes_per_launch": bytes_per_launch,
+        "kernel_us_mean": round(k1_mean, 2),
+        "kernel_us_median": round(_median(k1), 2),
+        "timing": (f"HIP events attached by the library to the kernel's dispatch, mean over "
+                   f"the {len(k1)} calls of the event pass after the timed calls"),
+    }
+    if not consistent:
+        out["note"] = (f"kernel 1 + kernel 2 ({k1_mean + k2_mean:.2f} us) exceed the time per "
+                       f"call ({us_per_call:.2f} us): no fraction reported")
+    if profile_us:
+        out["profile_kernel_us"] = profile_us
+        out["profile_frac"] = round(bytes_per_launch / (profile_us * 1e-6) / 1e9 /
+                                    PEAK_HBM_GBPS, 4)
+    return out
+
+
+def _oracle_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def threaded_oracle(work, chunks, threads: int) -> float:
+    """Run work(chunk) for every chunk on `threads` host threads (the oracle's
+    C calls release the GIL); returns the wall seconds."""
+    from concurrent.futures import ThreadPoolExecutor
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for f in [ex.submit(work, c) for c in chunks]:
+            f.result()
+    return time.perf_counter() - t0
+
+
+def _row_chunks(rows: int, parts: int):
+    step = -(-rows // parts)
+    return [(a, min(rows, a + step)) for a in range(0, rows, step)]
+
+
+def cpu_baseline(inp, rows: int, T: int, K: int, S: int, addend: bool):
+    """Time the FP64 oracle (as it is) on the first `rows` rows of the
+    workload, dX rows and their dW contribution, on every host core the
+    process may use (one thread per core, rows split into equal chunks);
+    also one thread on a slice, for the per-core rate."""
     import oracle
     from tests import gpu_harness as gh
 
     rows = min(rows, T)
     h = gh.host_rows(inp, list(range(rows)))
-    t0 = time.perf_counter()
-    oracle.dx(h["x"], h["w"], h["grad_proj"], h["grad_r"], h["r"], K, addend=h["addend"],
-              mode="tf32")
-    oracle.dw(h["x"], h["grad_proj"], mode="tf32")
-    dt = time.perf_counter() - t0
+
+    def work(span):
+        a, b = span
+        ad = h["addend"][a:b] if h["addend"] is not None else None
+        oracle.dx(h["x"][a:b], h["w"], h["grad_proj"][a:b], h["grad_r"][a:b], h["r"][a:b], K,
+                  addend=ad, mode="tf32")
+        oracle.dw(h["x"][a:b], h["grad_proj"][a:b], mode="tf32")
+
+    one_rows = min(rows, 64)
+    dt1 = threaded_oracle(work, [(0, one_rows)], 1)
+    cores = _oracle_threads()
+    dt = threaded_oracle(work, _row_chunks(rows, cores), cores)
     call_bytes, _ = algorithmic_bytes(T, K, S, addend)
-    frac = rows / T
-    us_per_call = dt / frac * 1e6
-    del np
     return {
-        "value": round(call_bytes * frac / dt / 1e9, 6),
+        "value": round(call_bytes * (rows / T) / dt / 1e9, 6),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": (f"first {rows} of {T} rows, all {K} columns: dX rows and their dW "
-                   f"contribution, TF32-mode FP64 oracle, one thread; {dt:.2f} s"),
-        "us_per_call_extrapolated": round(us_per_call, 1),
+                   f"contribution, TF32-mode FP64 oracle, {cores} threads (one per core of "
+                   f"the process's CPU affinity) on equal row chunks, {dt:.2f} s; one thread on "
+                   f"{one_rows} rows: {dt1:.2f} s"),
+        "one_thread_value": round(call_bytes * (one_rows / T) / dt1 / 1e9, 6),
+        "us_per_call_extrapolated": round(dt / (rows / T) * 1e6, 1),
     }
 
 
@@ -136,8 +312,8 @@ def split_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
     return dx, dw
 
 
-def run_split(args, wl, inp, plan, S, dx, dw, ws) -> dict:
-    """The split form: per step, the dX-only call then the dW-only call."""
+def run_split(args, wl, inp, plan, S, dx, dw, ws, settle) -> dict:
+    """The split form: per step the dX-only call then the dW-only call."""
     import torch
     from rms_backward_amd import mhcpb_execute_dw, mhcpb_execute_dx
     T, K = wl.T, wl.K
@@ -195,6 +371,7 @@ def run_split(args, wl, inp, plan, S, dx, dw, ws) -> dict:
             "dx_call_bytes": dx_bytes, "dw_call_bytes": dw_bytes,
             "dx_call_us": round(dx_us, 2), "dw_call_us": round(dw_us, 2),
             "timed_wall_s": round(wall, 4),
+            "device_settle": settle,
         },
         "roofline": {
             "bound": "hbm",
@@ -214,6 +391,7 @@ FORWARD_METRIC = ("forward map: µs/call and achieved HBM GB/s (% of peak) at "
 FORWARD_SOURCES = [os.path.join(ROOT, "rms_backward_amd", "csrc", n)
                    for n in ("mhcpb_forward.hip", "mhcpb_device.h")]
 FORWARD_COUNTERS_FILE = os.path.join(ROOT, "profiles", "forward_train_counters.json")
+FORWARD_TRACE_FILE = os.path.join(ROOT, "profiles", "forward_train_kernel_stats.json")
 
 
 def forward_bytes(T: int, K: int) -> tuple[int, int, int]:
@@ -229,53 +407,36 @@ def forward_bytes(T: int, K: int) -> tuple[int, int, int]:
 
 
 def forward_source_hash() -> str:
-    text = ""
-    for path in FORWARD_SOURCES:
-        with open(path, encoding="utf-8") as f:
-            text += f.read() + "\n"
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
-    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()[:16]
-
-
-def forward_traffic(workload: str):
-    """HBM bytes per pass-kernel launch from the committed counter summary,
-    if taken on the current forward source; otherwise None."""
-    try:
-        with open(FORWARD_COUNTERS_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256_16") != forward_source_hash():
-        return None
-    if rec.get("workload") != workload:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    return source_hash(FORWARD_SOURCES)
 
 
 def forward_cpu_baseline(x, w, rows: int, T: int, K: int):
-    """Time the FP64 oracle's forward (as it is, one thread) on `rows` rows."""
+    """Time the FP64 oracle's forward (as it is) on `rows` rows over the
+    host's cores (equal row chunks), and one thread on a slice."""
     import oracle
     rows = min(rows, T)
     xs = x[:rows].cpu().numpy()
     ws = w.cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.forward(xs, ws, eps=1e-6, mode="tf32")
-    dt = time.perf_counter() - t0
+    work = lambda span: oracle.forward(xs[span[0]:span[1]], ws, eps=1e-6, mode="tf32")
+    one_rows = min(rows, 64)
+    dt1 = threaded_oracle(work, [(0, one_rows)], 1)
+    cores = _oracle_threads()
+    dt = threaded_oracle(work, _row_chunks(rows, cores), cores)
     call_bytes, _, _ = forward_bytes(T, K)
-    frac = rows / T
     return {
-        "value": round(call_bytes * frac / dt / 1e9, 6),
+        "value": round(call_bytes * (rows / T) / dt / 1e9, 6),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"first {rows} of {T} rows, all {K} columns: proj and r, TF32-mode "
-                   f"FP64 oracle, one thread; {dt:.2f} s"),
-        "us_per_call_extrapolated": round(dt / frac * 1e6, 1),
+        "sample": (f"first {rows} of {T} rows, all {K} columns: proj and r, TF32-mode FP64 "
+                   f"oracle, {cores} threads on equal row chunks, {dt:.2f} s; one thread on "
+                   f"{one_rows} rows: {dt1:.2f} s"),
+        "one_thread_value": round(call_bytes * (one_rows / T) / dt1 / 1e9, 6),
+        "us_per_call_extrapolated": round(dt / (rows / T) * 1e6, 1),
     }
 
 
-def run_forward(args, wl) -> dict:
+def run_forward(args, wl, settle) -> dict:
     """The forward map: per step one mhcpb_forward call (the pass over X,
     then the sum of the tiles' partials)."""
     import torch
@@ -291,40 +452,21 @@ def run_forward(args, wl) -> dict:
     r = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
     ws = plan.alloc_forward_workspace("cuda")
     eps = 1e-6
-    call = lambda: plan.forward(x, w, eps, proj, r, ws)
+    stream = torch.cuda.current_stream()
+    call_ev = lambda a, b, c: mhcpb_forward_with_events(plan.handle, x, w, eps, proj, r, ws,
+                                                        ws.numel(), stream.cuda_stream, a, b, c)
+    call = lambda: call_ev(None, None, None)
+    load_kernels(args.stage)
+    settle.update(device_settle(SETTLE_MS if not args.no_settle else 0))
     for _ in range(args.warmup):
         call()
-    stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    us_per_call = e0.elapsed_time(e1) * 1e3 / args.steps
-
-    hev = HipEvents()
-    n = args.steps
-    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(n)]
-    torch.cuda.synchronize()
-    for a, b, c in evs:
-        mhcpb_forward_with_events(plan.handle, x, w, eps, proj, r, ws, ws.numel(),
-                                  stream.cuda_stream, a, b, c)
-    torch.cuda.synchronize()
-    k1_ms = [hev.elapsed_ms(a, b) for a, b, _ in evs]
-    k2_ms = [hev.elapsed_ms(b, c) for _, b, c in evs]
-    for trio in evs:
-        for e in trio:
-            hev.destroy(e)
-    k1_us = sum(k1_ms) / n * 1e3
-    k2_us = sum(k2_ms) / n * 1e3
+    us_per_call, wall = timed_calls(call, args.steps)
+    k1, k2 = event_pass(call_ev, max(args.steps, 100))
     call_bytes, k1_bytes, io_bytes = forward_bytes(T, K)
     gbps = call_bytes / (us_per_call * 1e-6) / 1e9
-    k1_gbps = k1_bytes / (k1_us * 1e-6) / 1e9
+    sha = forward_source_hash()
+    rec_c = _profile_record(FORWARD_COUNTERS_FILE, wl.name, sha)
+    rec_t = _profile_record(FORWARD_TRACE_FILE, wl.name, sha)
     return {
         "metric": FORWARD_METRIC,
         "value": round(gbps, 2),
@@ -346,19 +488,13 @@ def run_forward(args, wl) -> dict:
             "stage": "forward", "T": T, "K": K,
             "bytes_per_call": call_bytes,
             "bytes_per_call_without_partials": io_bytes,
-            "k1_us": round(k1_us, 2), "k2_us": round(k2_us, 2),
+            "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),
             "timed_wall_s": round(wall, 4),
+            "device_settle": settle,
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(k1_gbps, 2),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": forward_traffic(wl.name),
-            "kernel": "forward pass over X (forward_tiles, kernel 1)",
-            "bytes_per_launch": k1_bytes,
-        },
+        "roofline": roofline("forward pass over X (forward_tiles, kernel 1)", k1_bytes, k1, k2,
+                             us_per_call, rec_c.get("hbm_bytes_per_launch") if rec_c else None,
+                             rec_t.get("kernel1_avg_us") if rec_t else None),
         "_inputs": (x, w),
     }
 
@@ -368,6 +504,7 @@ RMS_METRIC = ("BF16 RMSNorm backward: µs/call and achieved HBM GB/s (% of peak)
 RMS_SOURCES = [os.path.join(ROOT, "rms_backward_amd", "csrc", n)
                for n in ("mhcpb_rmsnorm.hip", "mhcpb_device.h")]
 RMS_COUNTERS_FILE = os.path.join(ROOT, "profiles", "rmsnorm_train_counters.json")
+RMS_TRACE_FILE = os.path.join(ROOT, "profiles", "rmsnorm_train_kernel_stats.json")
 
 
 def rms_schedule(T: int, H: int) -> int:
@@ -392,33 +529,13 @@ def rms_bytes(T: int, H: int, w_f32: bool, residual: bool) -> tuple[int, int, in
 
 
 def rms_source_hash() -> str:
-    text = ""
-    for path in RMS_SOURCES:
-        with open(path, encoding="utf-8") as f:
-            text += f.read() + "\n"
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
-    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()[:16]
-
-
-def rms_traffic(workload: str):
-    """HBM bytes per rows-kernel launch from the committed counter summary, if
-    taken on the current source; otherwise None."""
-    try:
-        with open(RMS_COUNTERS_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256_16") != rms_source_hash():
-        return None
-    if rec.get("workload") != workload:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    return source_hash(RMS_SOURCES)
 
 
 def rms_cpu_baseline(inp, wl, min_seconds: float = 2.0):
-    """Time the FP64 oracle (as it is, one thread) on the whole workload,
-    repeated until at least `min_seconds` have passed."""
+    """Time the FP64 oracle (as it is) on the whole workload over the host's
+    cores (equal row chunks), repeated until at least `min_seconds` have
+    passed, and one thread on one call."""
     import oracle
     from tests import gpu_harness as gh
     g = gh.bf16_bits_np(inp["g"])
@@ -426,27 +543,35 @@ def rms_cpu_baseline(inp, wl, min_seconds: float = 2.0):
     w = inp["w"].float().cpu().numpy()
     rstd = inp["rstd"].cpu().numpy()
     res = gh.bf16_bits_np(inp["res"]) if inp.get("res") is not None else None
+
+    def work(span):
+        a, b = span
+        oracle.rmsnorm_backward(g[a:b], x[a:b], w, rstd[a:b],
+                                res_bits=res[a:b] if res is not None else None)
+
+    dt1 = threaded_oracle(work, [(0, wl.T)], 1)
+    cores = _oracle_threads()
+    chunks = _row_chunks(wl.T, cores)
     reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.rmsnorm_backward(g, x, w, rstd, res_bits=res)
+    dt = 0.0
+    while dt < min_seconds:
+        dt += threaded_oracle(work, chunks, cores)
         reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
     call_bytes, _, _ = rms_bytes(wl.T, wl.H, wl.w_f32, wl.residual)
     return {
         "value": round(call_bytes * reps / dt / 1e9, 6),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"the whole workload (all {wl.T} rows, dx and dw), FP64 oracle, one "
-                   f"thread, {reps} call(s) in {dt:.2f} s"),
+        "sample": (f"the whole workload (all {wl.T} rows, dx and dw), FP64 oracle, {cores} "
+                   f"threads on equal row chunks, {reps} call(s) in {dt:.2f} s; one thread: "
+                   f"{dt1:.2f} s per call"),
+        "one_thread_value": round(call_bytes / dt1 / 1e9, 6),
         "us_per_call_extrapolated": round(dt / reps * 1e6, 1),
     }
 
 
-def run_rmsnorm(args, wl) -> dict:
+def run_rmsnorm(args, wl, settle) -> dict:
     """The second workload: per step one mhcpb_rmsnorm_backward call (the rows
     kernel, then the fixed-order sum of the block partials)."""
     import torch
@@ -460,43 +585,23 @@ def run_rmsnorm(args, wl) -> dict:
     ws = torch.empty(max(1, m.mhcpb_rmsnorm_backward_workspace_bytes(T, H)), dtype=torch.uint8,
                      device="cuda")
     wd = m.MHCPB_DTYPE_F32 if wl.w_f32 else m.MHCPB_DTYPE_BF16
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    call = lambda: m.mhcpb_rmsnorm_backward(T, H, inp["g"], inp["x"], inp["w"], wd, inp["rstd"],
-                                            inp["res"], dx, dw, ws, ws.numel(), sh)
+    sh = torch.cuda.current_stream().cuda_stream
+    call_ev = lambda a, b, c: m.mhcpb_rmsnorm_backward_with_events(
+        T, H, inp["g"], inp["x"], inp["w"], wd, inp["rstd"], inp["res"], dx, dw, ws, ws.numel(),
+        sh, a, b, c)
+    call = lambda: call_ev(None, None, None)
+    load_kernels(args.stage)
+    settle.update(device_settle(SETTLE_MS if not args.no_settle else 0))
     for _ in range(args.warmup):
         call()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    us_per_call = e0.elapsed_time(e1) * 1e3 / args.steps
-
-    hev = HipEvents()
-    n = args.steps
-    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(n)]
-    torch.cuda.synchronize()
-    for a, b, c in evs:
-        m.mhcpb_rmsnorm_backward_with_events(T, H, inp["g"], inp["x"], inp["w"], wd, inp["rstd"],
-                                             inp["res"], dx, dw, ws, ws.numel(), sh, a, b, c)
-    torch.cuda.synchronize()
-    k1_ms = [hev.elapsed_ms(a, b) for a, b, _ in evs]
-    k2_ms = [hev.elapsed_ms(b, c) for _, b, c in evs]
-    for trio in evs:
-        for e in trio:
-            hev.destroy(e)
-    k1_us = sum(k1_ms) / n * 1e3
-    k2_us = sum(k2_ms) / n * 1e3
+    us_per_call, wall = timed_calls(call, args.steps)
+    k1, k2 = event_pass(call_ev, max(args.steps, 100))
     S = rms_schedule(T, H)
     call_bytes, k1_bytes, io_bytes = rms_bytes(T, H, wl.w_f32, wl.residual)
     gbps = call_bytes / (us_per_call * 1e-6) / 1e9
-    k1_gbps = k1_bytes / (k1_us * 1e-6) / 1e9
+    sha = rms_source_hash()
+    rec_c = _profile_record(RMS_COUNTERS_FILE, wl.name, sha)
+    rec_t = _profile_record(RMS_TRACE_FILE, wl.name, sha)
     return {
         "metric": RMS_METRIC,
         "value": round(gbps, 2),
@@ -520,19 +625,14 @@ def run_rmsnorm(args, wl) -> dict:
             "stage": "rmsnorm", "T": T, "H": H, "blocks": S,
             "bytes_per_call": call_bytes,
             "bytes_per_call_without_partials": io_bytes,
-            "k1_us": round(k1_us, 2), "k2_us": round(k2_us, 2),
+            "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),
             "timed_wall_s": round(wall, 4),
+            "device_settle": settle,
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(k1_gbps, 2),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": rms_traffic(wl.name),
-            "kernel": "RMSNorm backward rows (rmsnorm_bwd_rows, kernel 1)",
-            "bytes_per_launch": k1_bytes,
-        },
+        "roofline": roofline("RMSNorm backward rows (rmsnorm_bwd_rows, kernel 1)", k1_bytes, k1,
+                             k2, us_per_call,
+                             rec_c.get("hbm_bytes_per_launch") if rec_c else None,
+                             rec_t.get("kernel1_avg_us") if rec_t else None),
         "_inputs": inp,
     }
 
@@ -554,12 +654,14 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed calls before the timed ones (default: about 50 ms of "
-                         "calls, enough for the GPU clocks to settle: 500 for the stage, "
-                         "600 for the forward, 2000 for the RMSNorm backward)")
+                         "calls: 500 for the stage, 600 for the forward, 2000 for the RMSNorm "
+                         "backward)")
     ap.add_argument("--workload", default="train")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="rows of the workload the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="skip the ~300 ms of BF16 matrix products before the warm-up")
     ap.add_argument("--form", choices=("fused", "split"), default="fused",
                     help="fused: mhcpb_execute per step; split: mhcpb_execute_dx then "
                          "mhcpb_execute_dw per step (X read twice)")
@@ -590,12 +692,13 @@ def main(argv=None):
     from rms_backward_amd.wrapper import Plan
     from tests import gpu_harness as gh
 
+    settle = {}
     if args.stage == "rmsnorm":
         name = "rms_train" if args.workload == "train" else args.workload
         wl = workloads.RMS_WORKLOADS[name]
         print(f"bench: workload {wl.name} T={wl.T} H={wl.H} stage rmsnorm", file=sys.stderr,
               flush=True)
-        out = run_rmsnorm(args, wl)
+        out = run_rmsnorm(args, wl, settle)
         inp = out.pop("_inputs")
         if not args.no_cpu_baseline:
             print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
@@ -610,7 +713,7 @@ def main(argv=None):
     print(f"bench: workload {wl.name} T={T} K={K} stage {args.stage}", file=sys.stderr,
           flush=True)
     if args.stage == "forward":
-        out = run_forward(args, wl)
+        out = run_forward(args, wl, settle)
         x, w = out.pop("_inputs")
         if not args.no_cpu_baseline:
             print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -624,7 +727,9 @@ def main(argv=None):
     S = mhcpb_plan_split_count(plan.handle)
     dx, dw, ws = gh.alloc_outputs(T, K, plan, "cuda", poison=True)
     if args.form == "split":
-        out = run_split(args, wl, inp, plan, S, dx, dw, ws)
+        load_kernels(args.stage)
+        settle.update(device_settle(SETTLE_MS if not args.no_settle else 0))
+        out = run_split(args, wl, inp, plan, S, dx, dw, ws, settle)
         if not args.no_cpu_baseline:
             print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
             out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, T, K, S, wl.addend)
@@ -632,50 +737,22 @@ def main(argv=None):
             out["cpu_baseline"] = None
         print(json.dumps(out), flush=True)
         return 0
-    call = lambda: plan.execute(inp["x"], inp["w"], inp["grad_proj"], inp["grad_r"], inp["r"],
-                                dx, dw, ws, inp.get("addend"))
+    stream = torch.cuda.current_stream()
+    call_ev = lambda a, b, c: mhcpb_execute_with_events(
+        plan.handle, inp["x"], inp["w"], inp["grad_proj"], inp["grad_r"], inp["r"], dx, dw,
+        inp.get("addend"), ws, ws.numel(), stream.cuda_stream, a, b, c)
+    call = lambda: call_ev(None, None, None)
+    load_kernels(args.stage)
+    settle.update(device_settle(SETTLE_MS if not args.no_settle else 0))
     for _ in range(args.warmup):
         call()
-    torch.cuda.synchronize()
-
     # timed region: exactly `steps` calls
-    stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    us_per_call = e0.elapsed_time(e1) * 1e3 / args.steps
-
-    # per-kernel durations: the same calls, with HIP events the library attaches
-    # to the two dispatches on the launch stream (start and end of kernel 1, end
-    # of kernel 2)
-    hev = HipEvents()
-    n = args.steps
-    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(n)]
-    torch.cuda.synchronize()
-    for a, b, c in evs:
-        mhcpb_execute_with_events(plan.handle, inp["x"], inp["w"], inp["grad_proj"],
-                                  inp["grad_r"], inp["r"], dx, dw, inp.get("addend"), ws,
-                                  ws.numel(), stream.cuda_stream, a, b, c)
-    torch.cuda.synchronize()
-    k1_ms = [hev.elapsed_ms(a, b) for a, b, _ in evs]
-    k2_ms = [hev.elapsed_ms(b, c) for _, b, c in evs]
-    for trio in evs:
-        for e in trio:
-            hev.destroy(e)
-    k1_us = sum(k1_ms) / n * 1e3
-    k2_us = sum(k2_ms) / n * 1e3
+    us_per_call, wall = timed_calls(call, args.steps)
+    # kernel durations: the event pass right after
+    k1, k2 = event_pass(call_ev, max(args.steps, 100))
 
     call_bytes, k1_bytes = algorithmic_bytes(T, K, S, wl.addend)
     gbps = call_bytes / (us_per_call * 1e-6) / 1e9
-    k1_gbps = k1_bytes / (k1_us * 1e-6) / 1e9
-    traffic = measured_traffic(wl.name)
     out = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -698,19 +775,12 @@ def main(argv=None):
             "T": T, "K": K, "splits": S,
             "bytes_per_call": call_bytes,
             "bytes_per_call_without_partials": call_bytes - 2 * S * 24 * K * 4,
-            "k1_us": round(k1_us, 2), "k2_us": round(k2_us, 2),
+            "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),
             "timed_wall_s": round(wall, 4),
+            "device_settle": settle,
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(k1_gbps, 2),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": traffic,
-            "kernel": "projection (kernel 1)",
-            "bytes_per_launch": k1_bytes,
-        },
+        "roofline": roofline("projection (kernel 1)", k1_bytes, k1, k2, us_per_call,
+                             measured_traffic(wl.name), profiled_kernel1_us(wl.name)),
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)

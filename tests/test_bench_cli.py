@@ -39,3 +39,20 @@ def test_forward_and_rmsnorm_bytes():
     call, k1, io = bench.rms_bytes(4096, 5120, False, False)
     assert io == 4096 * 5120 * 2 * 3 + 5120 * 2 + 4096 * 4 + 5120 * 4
     assert call == io + 2 * S * 5120 * 4
+
+
+def test_roofline_refuses_events_that_do_not_fit_the_call():
+    # kernel 1 + kernel 2 beyond the measured time per call: no fraction
+    r = bench.roofline("k", 521437184, [114.7] * 20, [4.3] * 20, 101.3, None, None)
+    assert r["frac"] is None and r["achieved"] is None and "note" in r
+    r = bench.roofline("k", 521437184, [88.0] * 20, [4.0] * 20, 93.0, None, 89.9)
+    assert abs(r["frac"] - 521437184 / 88.0e-6 / 1e9 / 8000.0) < 1e-4
+    assert abs(r["profile_frac"] - 521437184 / 89.9e-6 / 1e9 / 8000.0) < 1e-4
+
+
+def test_oracle_row_chunks_cover_every_row_once():
+    for rows in (1, 7, 64, 2048, 4095):
+        for parts in (1, 3, 16, 128):
+            chunks = bench._row_chunks(rows, parts)
+            covered = [t for a, b in chunks for t in range(a, b)]
+            assert covered == list(range(rows)) and len(chunks) <= parts
