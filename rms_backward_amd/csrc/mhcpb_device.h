@@ -103,60 +103,83 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void *base, 
 // compiler cannot see that, and would otherwise wait for every outstanding
 // global load before any LDS read it cannot prove independent of the DMA.
 // All hot-loop LDS reads therefore go through these, followed by one
-// explicit lgkmcnt wait.
+// explicit lgkmcnt wait.  The template argument is a constant byte offset
+// that goes into the instruction's offset field (no address arithmetic).
+#define MHCPB_LDS_OFFSET_CHECK static_assert(kOff >= 0 && kOff < 65536, "LDS offset field")
+template <int kOff = 0>
 __device__ __forceinline__ f32x4 lds_read_b128(uint32_t addr) {
+    MHCPB_LDS_OFFSET_CHECK;
     f32x4 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
     return v;
 }
 
+template <int kOff = 0>
 __device__ __forceinline__ u32x4 lds_read_u128(uint32_t addr) {
+    MHCPB_LDS_OFFSET_CHECK;
     u32x4 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
     return v;
 }
 
+template <int kOff = 0>
 __device__ __forceinline__ uint32_t lds_read_u32(uint32_t addr) {
+    MHCPB_LDS_OFFSET_CHECK;
     uint32_t v;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
     return v;
 }
 
+template <int kOff = 0>
 __device__ __forceinline__ float lds_read_f32(uint32_t addr) {
+    MHCPB_LDS_OFFSET_CHECK;
     float v;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
     return v;
 }
 
+template <int kOff = 0>
 __device__ __forceinline__ u32x2 lds_read_u64(uint32_t addr) {
+    MHCPB_LDS_OFFSET_CHECK;
     u32x2 v;
-    asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr));
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
     return v;
 }
 
 // LDS writes of the operand staging and the counters, equally hidden from the
 // compiler's LDS-DMA ordering (they never touch the X ring); a wave waits for
 // them (lgkmcnt) before it passes a barrier or signals a counter.
+template <int kOff = 0>
 __device__ __forceinline__ void lds_write_u32(uint32_t addr, uint32_t v) {
-    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+    MHCPB_LDS_OFFSET_CHECK;
+    asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(kOff) : "memory");
 }
 
+template <int kOff = 0>
 __device__ __forceinline__ void lds_write_u128(uint32_t addr, u32x4 v) {
-    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+    MHCPB_LDS_OFFSET_CHECK;
+    asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(kOff) : "memory");
 }
 
+template <int kOff = 0>
 __device__ __forceinline__ void lds_write_u16(uint32_t addr, uint32_t v) {
-    asm volatile("ds_write_b16 %0, %1" ::"v"(addr), "v"(v) : "memory");
+    MHCPB_LDS_OFFSET_CHECK;
+    asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(kOff) : "memory");
 }
 
 // Writes the high 16 bits of v.
+template <int kOff = 0>
 __device__ __forceinline__ void lds_write_u16_hi(uint32_t addr, uint32_t v) {
-    asm volatile("ds_write_b16_d16_hi %0, %1" ::"v"(addr), "v"(v) : "memory");
+    MHCPB_LDS_OFFSET_CHECK;
+    asm volatile("ds_write_b16_d16_hi %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(kOff) : "memory");
 }
 
+template <int kOff = 0>
 __device__ __forceinline__ void lds_write_u64(uint32_t addr, u32x2 v) {
-    asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+    MHCPB_LDS_OFFSET_CHECK;
+    asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(kOff) : "memory");
 }
+#undef MHCPB_LDS_OFFSET_CHECK
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));

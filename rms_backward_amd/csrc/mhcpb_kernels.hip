@@ -17,9 +17,10 @@
 // TF32 product accumulated in FP32.  Each MFMA k slot pairs one part of one
 // operand with one part of the other: for dX the W side is held in registers
 // as packed (hi, lo) pairs and the P side is staged in LDS with each part
-// repeated, 4 MFMAs per 16x16 output block (24 j padded to 32); for dW the X
-// side is split in registers and the P side is staged per part, 4 MFMAs per
-// column group.  No operand needs a per-step shuffle.
+// repeated, 3 MFMAs per 16x16 output block (the 96 products of 24 j); for dW
+// the X side is split in registers and the P side is staged per part, twice
+// over, 4 MFMAs per column group (24 j padded to 32).  No operand needs a
+// per-step shuffle.
 //
 // X is streamed from HBM straight into LDS with buffer_load_dwordx4 ... lds,
 // a two-step ring per wave, so prefetching costs no registers; rows past the
@@ -28,6 +29,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 #include <mutex>
 
@@ -49,9 +51,9 @@ namespace {
 
 // Rows per step (one MFMA row block) and the LDS layouts of P.
 constexpr int kStepRows = 16;
-constexpr int kJPad = 32;                 // j slots per part, 24..31 zero
-constexpr int kPaStride = 2 * kJPad + 4;  // uint32 per row of the dX P operand
-constexpr int kPbJStride = 40;            // uint16 per j of the dW P operand (32 + 8 padding)
+constexpr int kPaStride = 2 * kProjCols + 4;  // uint32 per row of the dX P operand (4 padding)
+constexpr int kPbEntries = kProjCols + 1;     // j entries of the dW P operand, the last one zero
+constexpr int kPbJStride = 72;                // uint16 per j entry (64 + 8 padding)
 
 // The P of one step as it is stored in HBM, copied by LDS DMA: 16 rows of
 // grad_proj (32 floats each; the last 8 are never read from here), and one
@@ -63,36 +65,44 @@ struct RawStep {
 };
 
 // The P of one step in operand form (TF32 split into BF16 high and low parts):
-//  pa[row][part * 32 + j]: the part, duplicated in both halves of the word, as
+//  pa[row][part * 24 + j]: the part, duplicated in both halves of the word, as
 //      the dX product reads it (4 consecutive j per lane group);
-//  pb[j][g][part][r]: the part of row 4g + r, as the dW product reads it (both
-//      parts of 4 consecutive rows in 16 bytes);
+//  pb[j][g][part][h][r]: the part of row 4g + r, twice (h = 0, 1), as the dW
+//      product reads it: 16 bytes hold one part of 4 consecutive rows, once
+//      against the high and once against the low part of x.  Entry j = 24 is
+//      zero (cleared once) and stands for every padded j of that product;
 //  c[row]: grad_r / (r K).
-// Entries with j >= 24 are zero and never written after the first clear.
 struct alignas(16) StepP {
     uint32_t pa[kStepRows * kPaStride];
-    uint16_t pb[kJPad * kPbJStride];
+    uint16_t pb[kPbEntries * kPbJStride];
     float c[kStepRows];
 };
 
 // Operand slots in rotation, and how many steps ahead of its conversion the
 // producer requests the raw P of a step.
-constexpr int kSlots = 4;
-constexpr int kRawAhead = 2;
+#ifndef MHCPB_SLOTS
+#define MHCPB_SLOTS 4
+#endif
+#ifndef MHCPB_RAW_AHEAD
+#define MHCPB_RAW_AHEAD 2
+#endif
+constexpr int kSlots = MHCPB_SLOTS;
+constexpr int kRawAhead = MHCPB_RAW_AHEAD;
 constexpr int kRawBufs = kRawAhead + 1;
 
 // Kernel 1.  A workgroup has NW compute waves, which own the NW * 64 columns
 // of one column tile, and one producer wave.  The workgroup walks, one after
-// the other, the slabs s = sg, sg + G, sg + 2G, ... < S of its tile (sg = its
-// slab group): one unit of work per slab, each unit's rows in ascending
-// 16-row steps, and the steps of all its units form one continuous sequence
-// (global step k).  Per step a compute wave handles 16 rows x 64 columns:
+// the other, the consecutive slabs [sg S / G, (sg + 1) S / G) of its tile (sg
+// = its slab group, G <= S groups): one unit of work per slab, each unit's
+// rows in ascending 16-row steps, and the steps of all its units form one
+// continuous sequence (global step k).  Per step a compute wave handles 16 rows x 64 columns:
 // lane l (c = l % 16, g = l / 16) holds x[t0 + 4g + r][kw + 4c + i] for r, i
 // in 0..3.
 //  dX: C_i[e] = dX[t0 + 4g + e][kw + 4c + i] = c_t x + the products of the P
-//      parts (token t0 + l%16) with the W parts (column kw + 4c + i): per
-//      MFMA (P part p, j block b) lane group g covers j = 16b + 4g .. +3 times
-//      (W hi, W lo); 4 MFMAs cover the 96 products of 24 j (8 padded).
+//      parts (token t0 + l%16) with the W parts (column kw + 4c + i): in
+//      the MFMAs of P part p = 0, 1 lane group g covers j = 4g .. 4g + 3
+//      times (W hi, W lo); in the third, j = 16 + 4 (g % 2) .. +3 of P part
+//      g / 2, so 3 MFMAs cover the 96 products of 24 j.
 //  dW: acc[i][b][e] = sum over the slab's tokens of TF32(x) of column
 //      kw + 4(4g+e) + i times TF32(P[j]), j = 16 b + l%16: per MFMA (P part
 //      p), lane group g covers rows 4g .. 4g+3 times (x hi, x lo).  At the
@@ -100,14 +110,16 @@ constexpr int kRawBufs = kRawAhead + 1;
 //      accumulators restart from zero.
 //
 // Why one workgroup walks several slabs: a workgroup needs 6 waves and
-// 75 KB of LDS, so a CU holds one at a time; with one workgroup per (tile,
+// more than 64 KB of LDS, so a CU holds one at a time; with one workgroup per (tile,
 // slab) the supported profile (64 tiles x 8 slabs) ran as two rounds of 256
 // workgroups, each with its own start-up (the first X and W requests) and
 // drain.  With G = 4 slab groups the 256 workgroups each stream two slabs
 // back to back: the X of the next unit is requested while the last step of
-// the current one is computed and its partial is stored.  A column's dW sums
-// the same rows in the same order whatever the grouping, so the grouping
-// changes no bit of the result.
+// the current one is computed and its partial is stored.  Group 0 holds the
+// first slabs, so it can also add their partials up in the order kernel 2
+// would (one slab fewer to write and to read back at that profile).  A
+// column's dW sums the same rows in the same order whatever the grouping, so
+// the grouping changes no bit of the result.
 //
 // Memory pipeline.  Each compute wave streams its X through a two-step ring
 // in LDS: the DMA for step k + 1 is issued as soon as step k has arrived, so
@@ -150,23 +162,31 @@ __device__ __forceinline__ char *uniform_ptr(char *p) {
 // the last unit the slab has no rows, so every request of such a step falls
 // outside its buffer range.
 struct StepCursor {
-    int u;
+    int s;          // slab of the current unit
+    int s_end;      // one past the workgroup's last slab
     int j;
     int nst;        // steps of the current slab
     int slab_rows;  // rows of the current slab (0 past the last unit)
     int64_t row0;   // first row of the current slab
 };
 
+// First slab of slab group sg: the G groups split the S slabs into runs of
+// consecutive slabs, as even as they can be (G <= S, so none is empty).
+__host__ __device__ __forceinline__ int group_first_slab(int sg, int S, int G) {
+    return static_cast<int>((static_cast<int64_t>(sg) * S) / G);
+}
+
 __device__ __forceinline__ int slab_rows_at(int64_t row0, int64_t L, int64_t T) {
     const int64_t n = T - row0 < L ? T - row0 : L;
     return static_cast<int>(n > 0 ? n : 0);
 }
 
-__device__ __forceinline__ StepCursor cursor_start(int sg, int64_t L, int64_t T) {
+__device__ __forceinline__ StepCursor cursor_start(int sg, int S, int G, int64_t L, int64_t T) {
     StepCursor c;
-    c.u = 0;
+    c.s = group_first_slab(sg, S, G);
+    c.s_end = group_first_slab(sg + 1, S, G);
     c.j = 0;
-    c.row0 = static_cast<int64_t>(sg) * L;
+    c.row0 = static_cast<int64_t>(c.s) * L;
     c.slab_rows = slab_rows_at(c.row0, L, T);
     c.nst = (c.slab_rows + 15) / 16;
     return c;
@@ -174,18 +194,41 @@ __device__ __forceinline__ StepCursor cursor_start(int sg, int64_t L, int64_t T)
 
 // Advances by one step; returns true when the step left was the last of its
 // unit.
-__device__ __forceinline__ bool cursor_next(StepCursor &c, int G, int64_t L, int64_t T) {
+__device__ __forceinline__ bool cursor_next(StepCursor &c, int64_t L, int64_t T) {
     if (++c.j < c.nst) return false;
     c.j = 0;
-    ++c.u;
-    c.row0 += static_cast<int64_t>(G) * L;
-    c.slab_rows = slab_rows_at(c.row0, L, T);
+    ++c.s;
+    c.row0 += L;
+    c.slab_rows = c.s < c.s_end ? slab_rows_at(c.row0, L, T) : 0;
     c.nst = (c.slab_rows + 15) / 16;
     return true;
 }
 
 // Number of store instructions of one partial dW write (per compute wave).
 constexpr int kPartialStores = 6;
+
+// Compute waves per kernel-1 workgroup (64 columns each).
+constexpr int kProjectionWaves = 5;
+
+// The producer's writes of j = pj0 + E and pj0 + E + 1 (E even) of one row
+// into the dX operand: pa_hi points at the row's part 0 entry of j = pj0.
+template <int E>
+__device__ __forceinline__ void put_pa(uint32_t pa_hi, uint32_t a, uint32_t b) {
+    lds_write_u64<4 * E>(pa_hi, u32x2{dup_low_half(a), dup_low_half(b)});
+    lds_write_u64<4 * E + 4 * kProjCols>(pa_hi, u32x2{dup_high_half(a), dup_high_half(b)});
+}
+
+// The producer's writes of j = pj0 + E of one row into the dW operand:
+// pb0 points at pb[pj0][g][0][0][r]; 8 bytes lie between the two copies, 16
+// between the parts.
+template <int E>
+__device__ __forceinline__ void put_pb(uint32_t pb0, uint32_t v) {
+    constexpr int o = E * kPbJStride * 2;
+    lds_write_u16<o>(pb0, v);
+    lds_write_u16<o + 8>(pb0, v);
+    lds_write_u16_hi<o + 16>(pb0, v);
+    lds_write_u16_hi<o + 24>(pb0, v);
+}
 
 template <int NW, bool kAddend, bool kDX, bool kDW>
 __global__ __launch_bounds__((NW + 1) * kWave)
@@ -243,21 +286,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         }
     };
 
-    // The j = 24..31 entries of every operand slot are zero padding; the
-    // counters and the poison word start at zero.
-    constexpr int kPadJ = kJPad - kProjCols;
-    for (int i = tid; i < kSlots * kStepRows * 2 * kPadJ; i += kThreads) {
-        const int buf = i / (kStepRows * 2 * kPadJ);
-        const int k = i % (kStepRows * 2 * kPadJ);
-        const int row = k / (2 * kPadJ), rest = k % (2 * kPadJ);
-        const int part = rest / kPadJ, jj = kProjCols + rest % kPadJ;
-        lds_write_u32(lds_addr(pop[buf].pa + row * kPaStride + part * kJPad + jj), 0u);
-    }
-    for (int i = tid; i < kSlots * kPadJ * kPbJStride; i += kThreads) {
-        const int buf = i / (kPadJ * kPbJStride);
-        const int off = i % (kPadJ * kPbJStride);
-        lds_write_u16(lds_addr(pop[buf].pb + kProjCols * kPbJStride + off), 0u);
-    }
+    // The zero entry of the dW P operand of every slot; the counters and the
+    // poison word start at zero.
+    constexpr int kPbWords = kPbJStride / 2;  // uint32 per entry
+    for (int i = tid; i < kSlots * kPbWords; i += kThreads)
+        lds_write_u32(lds_addr(pop[i / kPbWords].pb + kProjCols * kPbJStride) + 4 * (i % kPbWords), 0u);
     if (tid < kSlots) {
         lds_write_u32(ready_addr + 4 * tid, 0u);
         lds_write_u32(consumed_addr + 4 * tid, 0u);
@@ -265,11 +298,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
     if (tid == 0) lds_write_u32(poison_addr, 0u);
 
     if (producer) {
-        StepCursor ahead = cursor_start(sg, L, T);
+        StepCursor ahead = cursor_start(sg, S, G, L, T);
 #pragma unroll
         for (int k = 0; k < kRawAhead; ++k) {
             issue_raw(k, ahead);
-            cursor_next(ahead, G, L, T);
+            cursor_next(ahead, L, T);
         }
         lds_barrier();
         // Lane = row * 4 + q converts j = 6q .. 6q + 5 of one row of P into
@@ -277,10 +310,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         // grad_r / (r K) of row lane in FP32 (zero past the slab end).
         const int prow = lane / 4;
         const int pj0 = 6 * (lane % 4);
-        StepCursor cur = cursor_start(sg, L, T);
+        StepCursor cur = cursor_start(sg, S, G, L, T);
         for (int k = 0; cur.slab_rows > 0; ++k) {
             issue_raw(k + kRawAhead, ahead);
-            cursor_next(ahead, G, L, T);
+            cursor_next(ahead, L, T);
             // The raw P of step k was requested before that of the kRawAhead
             // steps after it, kRawDma DMA instructions each.
             wait_vmcnt<kRawDma * kRawAhead>();
@@ -290,11 +323,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
             const RawStep &src = praw[k % kRawBufs];
             const StepP &d = pop[slot];
             const uint32_t ra = lds_addr(&src.p[0]) + static_cast<uint32_t>((prow * kProjStride + pj0) * 4);
-            u32x2 v0 = lds_read_u64(ra), v1 = lds_read_u64(ra + 8), v2 = lds_read_u64(ra + 16);
+            u32x2 v0 = lds_read_u64(ra), v1 = lds_read_u64<8>(ra), v2 = lds_read_u64<16>(ra);
             float grv = 0.f, rv = 1.f;
             if constexpr (kDX) {
-                grv = lds_read_f32(lds_addr(&src.gr[lane]));
-                rv = lds_read_f32(lds_addr(&src.r[lane]));
+                const uint32_t rl = lds_addr(&src) + 4 * lane;
+                grv = lds_read_f32<offsetof(RawStep, gr)>(rl);
+                rv = lds_read_f32<offsetof(RawStep, r)>(rl);
             }
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(grv), "+v"(rv)::"memory");
@@ -303,25 +337,23 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
 #pragma unroll
             for (int e = 0; e < 6; ++e) pk[e] = tf32_split_packed_p(__uint_as_float(vv[e]));
             const uint32_t pa_hi = lds_addr(d.pa + prow * kPaStride + pj0);
-            const uint32_t pa_lo = pa_hi + kJPad * 4;
-#pragma unroll
-            for (int e = 0; e < 6; e += 2) {
-                lds_write_u64(pa_hi + 4 * e, u32x2{dup_low_half(pk[e]), dup_low_half(pk[e + 1])});
-                lds_write_u64(pa_lo + 4 * e, u32x2{dup_high_half(pk[e]), dup_high_half(pk[e + 1])});
-            }
-            const uint32_t pb0 = lds_addr(d.pb + pj0 * kPbJStride + (prow / 4) * 8 + prow % 4);
-            const uint32_t pb1 = pb0 + 4 * 2;
-#pragma unroll
-            for (int e = 0; e < 6; ++e) {
-                lds_write_u16(pb0 + e * kPbJStride * 2, pk[e]);
-                lds_write_u16_hi(pb1 + e * kPbJStride * 2, pk[e]);
-            }
+            put_pa<0>(pa_hi, pk[0], pk[1]);
+            put_pa<2>(pa_hi, pk[2], pk[3]);
+            put_pa<4>(pa_hi, pk[4], pk[5]);
+            // pb[j][g][part][h][r] with g = prow / 4, r = prow % 4.
+            const uint32_t pb0 = lds_addr(d.pb + pj0 * kPbJStride + (prow / 4) * 16 + prow % 4);
+            put_pb<0>(pb0, pk[0]);
+            put_pb<1>(pb0, pk[1]);
+            put_pb<2>(pb0, pk[2]);
+            put_pb<3>(pb0, pk[3]);
+            put_pb<4>(pb0, pk[4]);
+            put_pb<5>(pb0, pk[5]);
             if (kDX && lane < kStepRows) {
                 const bool in_slab = kStepRows * cur.j + lane < cur.slab_rows;
                 lds_write_u32(lds_addr(d.c + lane), __float_as_uint(in_slab ? grv / (rv * kf) : 0.f));
             }
             lds_signal(ready_addr + 4 * slot, lane);
-            cursor_next(cur, G, L, T);
+            cursor_next(cur, L, T);
         }
         // Drain the copies still in flight before the workgroup's LDS can be
         // released.
@@ -333,6 +365,20 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
     const int64_t kw = static_cast<int64_t>(tile) * (NW * 64) + wave * 64;
     const int kwi = static_cast<int>(kw);  // kw < K + NW * 64
     const int64_t col = kw + 4 * c16;      // first of this lane's 4 columns
+    // Byte offsets, within an operand slot, of this lane's P operands: the
+    // RMS coefficients of rows 4g .. 4g + 3; the dX P operands of token c16
+    // (part 0 of j = 4g .. 4g + 3, part 1 4 kProjCols bytes on, and the
+    // third MFMA's j = 16 + 4 (g % 2) .. +3 of part g / 2); the dW P operands
+    // of j = c16 and of j = 16 + c16 or, past j = 23, the zero entry (part 1
+    // 16 bytes on).
+    const uint32_t off_c = static_cast<uint32_t>(offsetof(StepP, c) + 16 * g);
+    const uint32_t off_pa = static_cast<uint32_t>((c16 * kPaStride + 4 * g) * 4);
+    const uint32_t off_pa3 =
+        static_cast<uint32_t>((c16 * kPaStride + (g >> 1) * kProjCols + 16 + 4 * (g & 1)) * 4);
+    const uint32_t off_pb[2] = {
+        static_cast<uint32_t>(offsetof(StepP, pb) + (c16 * kPbJStride + 16 * g) * 2),
+        static_cast<uint32_t>(offsetof(StepP, pb) +
+                              ((c16 < kProjCols - 16 ? 16 + c16 : kProjCols) * kPbJStride + 16 * g) * 2)};
     const bool active = col < K;
     // A step is addressed through one buffer resource per tensor, based at
     // row t0 and column kw, whose range ends at the slab end or 16 rows on,
@@ -379,31 +425,32 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
     // of steps 0 and 1 (both ring stages are free at the start), so that the
     // wait for W below does not wait for X, and two steps stream in while the
     // prologue runs.
-    float4 wraw[2][4] = {};  // [j block][e]: W[16 b + 4 g + e][col .. col + 3]
+    // [j block][e]: W[jb + e][col .. col + 3] with jb = 4 g in block 0 and
+    // 16 + 4 (g % 2) in block 1 (j = 16..23 twice, once per P part).
+    float4 wraw[2][4] = {};
     if constexpr (kDX) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int jj = 16 * b + 4 * g + e;
-                wraw[b][e] = (active && jj < kProjCols)
-                                 ? *reinterpret_cast<const float4 *>(w + jj * K + col)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+                const int jj = (b == 0 ? 4 * g : 16 + 4 * (g & 1)) + e;
+                wraw[b][e] = active ? *reinterpret_cast<const float4 *>(w + jj * K + col)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
             }
     }
     compiler_fence();
-    StepCursor nxt = cursor_start(sg, L, T);  // the next step whose X is requested
+    StepCursor nxt = cursor_start(sg, S, G, L, T);  // the next step whose X is requested
     issue_x(nxt, 0);
-    cursor_next(nxt, G, L, T);
+    cursor_next(nxt, L, T);
     issue_x(nxt, 1);
-    cursor_next(nxt, G, L, T);
+    cursor_next(nxt, L, T);
     compiler_fence();
     // Padding and counters visible (the producer passes the same barrier).
     lds_barrier();
 
     // W side of the dX product: for column variant i and j block b the lane
-    // holds the packed (hi | lo << 16) TF32 split of W[j][col + i] for
-    // j = 16b + 4g .. 16b + 4g + 3 (zero for j >= 24).
+    // holds the packed (hi | lo << 16) TF32 split of W[j][col + i] for the
+    // four j of wraw[b].
     u32x4 bw[4][2] = {};
 #pragma unroll
     for (int b = 0; b < 2 && kDX; ++b) {
@@ -463,7 +510,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         }
     };
 
-    StepCursor cur = cursor_start(sg, L, T);  // the step being computed
+    StepCursor cur = cursor_start(sg, S, G, L, T);  // the step being computed
     char *d_cur = reinterpret_cast<char *>(dx + cur.row0 * K + kw);
     const char *a_cur = reinterpret_cast<const char *>(addend + cur.row0 * K + kw);
     // The ready count of a step's slot is read one step early, so that its
@@ -478,8 +525,19 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
     char *d_prev = d_cur;
     int d_range_prev = 0;
     bool bad = false;           // this workgroup's results can no longer be trusted
-    bool after_unit = false;    // the previous step ended a unit (its partial was stored)
-    int last_unit_s = sg;       // slab of the unit whose partial is still to be stored
+    bool stored = false;        // the previous step ended a unit and stored its partial
+    int last_unit_s = cur.s;    // slab of the unit whose partial is still to be stored
+    // Slab group 0 adds the partials of its slabs (0, 1, ...) up in
+    // registers, in that order, and stores only the sum, into its last slab:
+    // the first adds of kernel 2's ascending order, the same FP32 operations
+    // in the same order, done before the partials leave the CU (-0 is the
+    // identity of x + y, signed zeros included).
+    const bool fold = sg == 0;
+    f32x4 pref[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) pref[i][jb] = f32x4{-0.f, -0.f, -0.f, -0.f};
     for (int k = 0; cur.slab_rows > 0; ++k) {
         const int rows_left = cur.slab_rows - kStepRows * cur.j;
         // From the top of the step until the next X is requested the wave
@@ -496,25 +554,26 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
             bad = true;
             lds_raise_poison(poison_addr, lane);
         }
-        const StepP &cur_p = pop[slot];
         // The P operands of this step are requested first: the RMS
         // coefficients of rows 4g..4g+3, the dX P operands (token c16, part
         // p, j = 16b + 4g .. +3) and the dW P operands (part p, j = 16b +
         // c16, rows 4g .. 4g+3; entries j >= 24 are zero).
         f32x4 cc = {};
-        u32x4 pa[2][2] = {};  // [part][block]
-        u32x4 pbv[2] = {};    // [block]: part 0 in .xy, part 1 in .zw
-        if constexpr (kDX) cc = lds_read_b128(lds_addr(cur_p.c + 4 * g));
+        u32x4 pa[3] = {};     // parts 0 and 1 of j = 4g .. 4g + 3, then block 1
+        u32x4 pb[2][2] = {};  // [part][block]
+        const uint32_t slot_base = lds_addr(&pop[slot]);
+        if constexpr (kDX) {
+            cc = lds_read_b128(slot_base + off_c);
+            pa[0] = lds_read_u128(slot_base + off_pa);
+            pa[1] = lds_read_u128<4 * kProjCols>(slot_base + off_pa);
+            pa[2] = lds_read_u128(slot_base + off_pa3);
+        }
+        if constexpr (kDW) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if constexpr (kDX) {
-#pragma unroll
-                for (int p = 0; p < 2; ++p)
-                    pa[p][b] = lds_read_u128(
-                        lds_addr(cur_p.pa + c16 * kPaStride + p * kJPad + 16 * b + 4 * g));
+            for (int b = 0; b < 2; ++b) {
+                pb[0][b] = lds_read_u128(slot_base + off_pb[b]);
+                pb[1][b] = lds_read_u128<16>(slot_base + off_pb[b]);
             }
-            if constexpr (kDW)
-                pbv[b] = lds_read_u128(lds_addr(cur_p.pb + (16 * b + c16) * kPbJStride + 8 * g));
         }
         // Then wait for this step's X and read it (4 rows).  Step k >= 1
         // issues, in this order: [4 addend loads] 4 X DMA (for step k + 1),
@@ -523,7 +582,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         // unit]; step 0 issues no X (the prologue requested steps 0 and 1,
         // after the W loads).  So after the X of step k come at most 4 dX
         // stores (of step k - 1, or of step k - 2 when deferred; none without
-        // dX) and, when step k - 1 ended a unit, that unit's partial stores;
+        // dX) and, when step k - 1 ended a unit and stored its partial, those
+        // stores;
         // after the X of step 0 the X of step 1: vmcnt(4), or vmcnt(0) for
         // the later steps of the dW-only form, plus kPartialStores after a
         // unit's end, covers it.  With deferred stores step 0 stores nothing,
@@ -533,7 +593,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         // end are still requested (they read zeros; their stores fall outside
         // the range), which keeps every step's count identical.
         const bool four = k == 0 || (kDX && !(kDefer && k == 1));
-        if (!after_unit || !kDW) {
+        if (!stored || !kDW) {
             if (four)
                 wait_vmcnt<4>();
             else
@@ -546,8 +606,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         }
         const uint32_t xa = ring_base + static_cast<uint32_t>((((k & 1) * 4) * kWave + lane) * 16);
         f32x4 xc[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) xc[rr] = lds_read_b128(xa + rr * kWave * 16);
+        xc[0] = lds_read_b128(xa);
+        xc[1] = lds_read_b128<kWave * 16>(xa);
+        xc[2] = lds_read_b128<2 * kWave * 16>(xa);
+        xc[3] = lds_read_b128<3 * kWave * 16>(xa);
         // The poison word is read after the slot: a producer that gave up
         // raised it before it overwrote a slot.
         uint32_t pois = lds_read_u32(poison_addr);
@@ -556,17 +618,16 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         if constexpr (kDX && kDW)
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
-                           "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]), "+v"(pa[1][1]),
-                           "+v"(pbv[0]), "+v"(pbv[1]), "+v"(pois)::"memory");
+                           "+v"(pa[0]), "+v"(pa[1]), "+v"(pa[2]), "+v"(pb[0][0]), "+v"(pb[0][1]),
+                           "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(pois)::"memory");
         else if constexpr (kDX)
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
-                           "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(pa[1][0]),
-                           "+v"(pa[1][1]), "+v"(pois)::"memory");
+                           "+v"(pa[0]), "+v"(pa[1]), "+v"(pa[2]), "+v"(pois)::"memory");
         else
             asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(pbv[0]),
-                           "+v"(pbv[1]), "+v"(pois)::"memory");
+                         : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(pb[0][0]),
+                           "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(pois)::"memory");
         bad = bad || __builtin_amdgcn_readfirstlane(pois) != 0;
         lds_signal(consumed_addr + 4 * slot, lane);
         uint2 av[4] = {};
@@ -582,7 +643,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         compiler_fence();
         if (k > 0) {
             issue_x(nxt, (k + 1) & 1);
-            cursor_next(nxt, G, L, T);
+            cursor_next(nxt, L, T);
         }
         compiler_fence();
         __builtin_amdgcn_s_setprio(0);
@@ -597,13 +658,6 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         compiler_fence();
 
         const float ce[4] = {cc[0], cc[1], cc[2], cc[3]};
-        u32x4 pb[2][2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                pb[p][b] = p == 0 ? u32x4{pbv[b].x, pbv[b].y, pbv[b].x, pbv[b].y}
-                                  : u32x4{pbv[b].z, pbv[b].w, pbv[b].z, pbv[b].w};
 
         uint32_t packed[4][2];  // dX of row 4g + r, columns (0,1) and (2,3)
 #pragma unroll
@@ -613,10 +667,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
             f32x4 acc = {};
             if constexpr (kDX) {
                 acc = f32x4{ce[0] * xc[0][i], ce[1] * xc[1][i], ce[2] * xc[2][i], ce[3] * xc[3][i]};
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int p = 0; p < 2; ++p) acc = mfma(pa[p][b], bw[i][b], acc);
+                acc = mfma(pa[0], bw[i][0], acc);
+                acc = mfma(pa[1], bw[i][0], acc);
+                acc = mfma(pa[2], bw[i][1], acc);
             }
 
             // dW: x of column variant i split into BF16 hi/lo, packed
@@ -672,8 +725,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         d_cur += kStepRows * row_bytes_d;
         if constexpr (kAddend) a_cur += kStepRows * row_bytes_d;
         ready_seen = lds_read_u32(ready_addr + 4 * ((k + 1) % kSlots));
-        const int s_done = sg + cur.u * G;
-        after_unit = cursor_next(cur, G, L, T);
+        const int s_done = cur.s;
+        const bool after_unit = cursor_next(cur, L, T);
         if (after_unit) {
             d_cur = reinterpret_cast<char *>(dx + cur.row0 * K + kw);
             if constexpr (kAddend) a_cur = reinterpret_cast<const char *>(addend + cur.row0 * K + kw);
@@ -681,17 +734,34 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         // At the end of a unit that is not the last, its partial dW goes to
         // workspace slab s_done while the X of the next unit is already in
         // flight (through ring stage k & 1, which holds no request until the
-        // next step); the accumulators restart from zero.  The last unit's
-        // partial is stored after the drain below.
+        // next step), or, in group 0, into the running sum; the accumulators
+        // restart from zero.  The last unit's partial (group 0: the sum) is
+        // stored after the drain below.
+        stored = false;
         if (kDW && after_unit) {
-            if (cur.slab_rows > 0) {
+            const bool last = cur.slab_rows == 0;
+            if (fold) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int jb = 0; jb < 2; ++jb) pref[i][jb] += accw[i][jb];
+            } else if (!last) {
                 store_partial(s_done, ring_base + static_cast<uint32_t>((k & 1) * 4 * kWave * 16), bad);
+                stored = true;
+            }
+            if (last) {
+                last_unit_s = s_done;
+                if (fold) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int jb = 0; jb < 2; ++jb) accw[i][jb] = pref[i][jb];
+                }
+            } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int jb = 0; jb < 2; ++jb) accw[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            } else {
-                last_unit_s = s_done;
             }
         }
     }
@@ -713,50 +783,64 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
     if constexpr (kDW) store_partial(last_unit_s, ring_base, bad);
 }
 
-// dW[i] = (((ws[0][i] + ws[1][i]) + ws[2][i]) + ...), four elements (one
-// quad) per column group; a thread takes kReduceQuads quads spaced by the
-// grid's thread count, and requests eight slabs of each of them before it
-// adds them in order, so that 8 x kReduceQuads loads are in flight.
-#ifndef MHCPB_K2_QPT
-#define MHCPB_K2_QPT 1
+// dW[i] = (((ws[f][i] + ws[f + 1][i]) + ws[f + 2][i]) + ...) + ws[S - 1][i]:
+// slab f holds the sum of slabs 0 .. f, added in that order by kernel 1's
+// slab group 0, so this is the ascending sum over every slab.  Four
+// elements (one quad) per thread; a thread requests eight slabs of its quad
+// before it adds them in order, so that eight loads are in flight.
+//
+// The quads are dealt to blocks by kernel 1's column tiles: block b takes the
+// tiles t with t % 8 == b % 8, which are the tiles whose partials kernel 1's
+// workgroups on the same XCD wrote when workgroups go to the 8 XCDs
+// round-robin by index and the tile count is a multiple of 8 (the supported
+// profile), so that the slabs stored last are still in that XCD's L2.  Any
+// other placement gives the same sums, only slower.
+#ifndef MHCPB_K2_NT
+#define MHCPB_K2_NT 1
 #endif
 constexpr int kReduceBatch = 8;
-constexpr int kReduceQuads = MHCPB_K2_QPT;
-__global__ __launch_bounds__(256) void reduce_slabs(const float *__restrict__ ws,
-                                                    float *__restrict__ dw, int S,
-                                                    int64_t n4) {
-    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(ws);
-    f32x4 a[kReduceQuads];
-#pragma unroll
-    for (int q = 0; q < kReduceQuads; ++q) {
-        const int64_t i = i0 + q * nthreads;
-        a[q] = i < n4 ? __builtin_nontemporal_load(src + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
-        f32x4 b[kReduceQuads][kReduceBatch];
+constexpr int kXcds = 8;
+#ifndef MHCPB_K2_THREADS
+#define MHCPB_K2_THREADS 256
+#endif
+constexpr int kReduceThreads = MHCPB_K2_THREADS;
+__device__ __forceinline__ f32x4 load_slab_quad(const f32x4 *p) {
+    if constexpr (MHCPB_K2_NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+__global__ __launch_bounds__(kReduceThreads) void reduce_slabs(const float *__restrict__ ws,
+                                                               float *__restrict__ dw, int first,
+                                                               int S, int64_t K, int tile_quads,
+                                                               int tiles) {
+    const int xcd = static_cast<int>(blockIdx.x) % kXcds;
+    // Quad q of this XCD's share: tile xcd + 8 (q / per_tile), row j, column
+    // quad c4 of the tile.
+    const int q = (static_cast<int>(blockIdx.x) / kXcds) * kReduceThreads + static_cast<int>(threadIdx.x);
+    const int per_tile = kProjCols * tile_quads;
+    const int t = xcd + kXcds * (q / per_tile);
+    const int qt = q % per_tile;
+    const int j = qt / tile_quads;
+    const int64_t k4 = K / 4;
+    const int64_t c4 = static_cast<int64_t>(t) * tile_quads + qt % tile_quads;
+    if (t >= tiles || c4 >= k4) return;
+    const int64_t n4 = kProjCols * k4;  // quads per slab
+    const int64_t i = j * k4 + c4;
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(ws) + i;
+    f32x4 a = load_slab_quad(src + first * n4);
+    for (int s0 = first + 1; s0 < S; s0 += kReduceBatch) {
+        f32x4 b[kReduceBatch];
         // Past the last slab the addend is -0, which leaves every sum as it
         // is (x + -0 == x, signed zeros included).
 #pragma unroll
-        for (int q = 0; q < kReduceQuads; ++q)
-#pragma unroll
-            for (int u = 0; u < kReduceBatch; ++u) {
-                const int64_t i = i0 + q * nthreads;
-                b[q][u] = (s0 + u < S && i < n4)
-                              ? __builtin_nontemporal_load(src + static_cast<int64_t>(s0 + u) * n4 + i)
+        for (int u = 0; u < kReduceBatch; ++u)
+            b[u] = s0 + u < S ? load_slab_quad(src + static_cast<int64_t>(s0 + u) * n4)
                               : f32x4{-0.f, -0.f, -0.f, -0.f};
-            }
 #pragma unroll
-        for (int q = 0; q < kReduceQuads; ++q)
-#pragma unroll
-            for (int u = 0; u < kReduceBatch; ++u) a[q] += b[q][u];
+        for (int u = 0; u < kReduceBatch; ++u) a += b[u];
     }
-#pragma unroll
-    for (int q = 0; q < kReduceQuads; ++q) {
-        const int64_t i = i0 + q * nthreads;
-        if (i < n4) reinterpret_cast<f32x4 *>(dw)[i] = a[q];
-    }
+    reinterpret_cast<f32x4 *>(dw)[i] = a;
 }
 
 // Slab groups G of kernel 1: enough workgroups (tiles x G) for one per CU of
@@ -802,19 +886,26 @@ hipError_t launch_projection_t(const Plan &p, const Args &a, Outputs out, hipStr
 }  // namespace
 
 // Launch shape, a performance choice only: each column's dW is summed in the
-// same order whatever the workgroup width, so every shape gives the same bits.
-// Five compute waves and the producer make two workgroups per CU exactly
-// three waves per SIMD; at K = 20480 with 8 splits the grid is one full round
-// of two workgroups per CU on 256 CUs.
+// same order whatever the workgroup width or slab grouping, so every shape
+// gives the same bits.  Five compute waves and the producer per workgroup, one
+// workgroup per CU; at K = 20480 with 8 splits, 64 column tiles x 4 slab
+// groups fill 256 CUs once.
 hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
-    return launch_projection_t<5>(p, a, out, stream, start, stop);
+    return launch_projection_t<kProjectionWaves>(p, a, out, stream, start, stop);
 }
 
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop) {
-    const int64_t n4 = kProjCols * p.K / 4;
-    const unsigned blocks = static_cast<unsigned>((n4 + 256 * kReduceQuads - 1) / (256 * kReduceQuads));
-    return launch(reduce_slabs, dim3(blocks), dim3(256), stream, nullptr, stop, a.ws, a.dw, p.S, n4);
+    // The column tiles of kernel 1 (kProjectionWaves * 64 columns each).
+    constexpr int tile_quads = kProjectionWaves * kWave / 4;
+    const int tiles = static_cast<int>((p.K + 4 * tile_quads - 1) / (4 * tile_quads));
+    const int64_t per_xcd = static_cast<int64_t>((tiles + kXcds - 1) / kXcds) * kProjCols * tile_quads;
+    const unsigned blocks =
+        static_cast<unsigned>(kXcds * ((per_xcd + kReduceThreads - 1) / kReduceThreads));
+    // Slab group 0 of kernel 1 leaves the sum of its slabs in its last one.
+    const int first = group_first_slab(1, p.S, slab_groups(tiles, p.S)) - 1;
+    return launch(reduce_slabs, dim3(blocks), dim3(kReduceThreads), stream, nullptr, stop, a.ws,
+                  a.dw, first, p.S, p.K, tile_quads, tiles);
 }
 
 // Static workspace for callers that cannot allocate (mhcpb_execute_noalloc).
