@@ -50,14 +50,46 @@ TRACE_FILE = os.path.join(ROOT, "profiles", "projection_train_kernel_stats.json"
 SETTLE_MS = 300.0
 
 
+def partial_slabs_moved(K: int, S: int) -> int:
+    """Workspace slabs that kernel 1 writes and kernel 2 reads: S, less the
+    ones kernel 1's slab group 0 adds up before it stores them (its run of
+    S // G consecutive slabs leaves one).  G follows kernel 1's launch shape:
+    320-column tiles, min(S, 256 // tiles) slab groups, at least one."""
+    tiles = -(-K // 320)
+    groups = max(1, min(S, 256 // tiles))
+    return S - (S // groups - 1)
+
+
 def algorithmic_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
-    """(whole call, kernel 1) algorithmic bytes."""
+    """(whole call, kernel 1) algorithmic bytes: X read and dX written once
+    (and the addend read), W, P, grad_r and r read, the partial slabs moved
+    written by kernel 1 and read by kernel 2, and dW written."""
     big = T * K * 4 + T * K * 2 + (T * K * 2 if addend else 0)
     small = 24 * K * 4 + 24 * T * 4 + 2 * T * 4
-    slabs = S * 24 * K * 4
+    slabs = partial_slabs_moved(K, S) * 24 * K * 4
     k1 = big + small + slabs
     call = k1 + slabs + 24 * K * 4
     return call, k1
+
+
+def cycling(calls_ev):
+    """Given one call (taking three event handles) per buffer set, returns
+    (call_ev, call) that go through the sets in turn."""
+    state = [0]
+
+    def call_ev(a, b, c):
+        f = calls_ev[state[0] % len(calls_ev)]
+        state[0] += 1
+        return f(a, b, c)
+
+    return call_ev, (lambda: call_ev(None, None, None))
+
+
+def buffer_sets_note(n: int) -> str:
+    if n <= 1:
+        return "one set of inputs and outputs, the same buffers every call"
+    return (f"the calls cycle through {n} copies of the large inputs and outputs, so that no "
+            f"call finds the previous call's data in the 256 MB Infinity Cache")
 
 
 def source_hash(paths) -> str:
@@ -308,7 +340,7 @@ def cpu_baseline(inp, rows: int, T: int, K: int, S: int, addend: bool):
 def split_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
     """Algorithmic bytes of (mhcpb_execute_dx, mhcpb_execute_dw) calls."""
     dx = T * K * 4 + T * K * 2 + (T * K * 2 if addend else 0) + 24 * K * 4 + 24 * T * 4 + 2 * T * 4
-    dw = T * K * 4 + 24 * T * 4 + 2 * S * 24 * K * 4 + 24 * K * 4
+    dw = T * K * 4 + 24 * T * 4 + 2 * partial_slabs_moved(K, S) * 24 * K * 4 + 24 * K * 4
     return dx, dw
 
 
@@ -367,6 +399,7 @@ def run_split(args, wl, inp, plan, S, dx, dw, ws, settle) -> dict:
                          f"{wl.hidden} (K={K}); split form (dX call, then dW call)"
                          + (", BF16 addend" if wl.addend else "")),
             "form": "split", "T": T, "K": K, "splits": S,
+            "buffer_sets": 1, "buffers": buffer_sets_note(1),
             "bytes_per_step": dx_bytes + dw_bytes,
             "dx_call_bytes": dx_bytes, "dw_call_bytes": dw_bytes,
             "dx_call_us": round(dx_us, 2), "dw_call_us": round(dw_us, 2),
@@ -453,9 +486,12 @@ def run_forward(args, wl, settle) -> dict:
     ws = plan.alloc_forward_workspace("cuda")
     eps = 1e-6
     stream = torch.cuda.current_stream()
-    call_ev = lambda a, b, c: mhcpb_forward_with_events(plan.handle, x, w, eps, proj, r, ws,
-                                                        ws.numel(), stream.cuda_stream, a, b, c)
-    call = lambda: call_ev(None, None, None)
+    n_sets = max(1, args.buffer_sets)
+    xsets = [x] + [x.clone() for _ in range(n_sets - 1)]
+    call_ev, call = cycling([
+        (lambda a, b, c, xs=xs: mhcpb_forward_with_events(plan.handle, xs, w, eps, proj, r, ws,
+                                                          ws.numel(), stream.cuda_stream, a, b, c))
+        for xs in xsets])
     load_kernels(args.stage)
     settle.update(device_settle(SETTLE_MS if not args.no_settle else 0))
     for _ in range(args.warmup):
@@ -486,6 +522,7 @@ def run_forward(args, wl, settle) -> dict:
             "workload": (f"{wl.name} forward: T={T} tokens, {wl.streams} streams x hidden "
                          f"{wl.hidden} (K={K}); X, W FP32 in, proj [T, 32] and r FP32 out"),
             "stage": "forward", "T": T, "K": K,
+            "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets),
             "bytes_per_call": call_bytes,
             "bytes_per_call_without_partials": io_bytes,
             "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),
@@ -586,10 +623,15 @@ def run_rmsnorm(args, wl, settle) -> dict:
                      device="cuda")
     wd = m.MHCPB_DTYPE_F32 if wl.w_f32 else m.MHCPB_DTYPE_BF16
     sh = torch.cuda.current_stream().cuda_stream
-    call_ev = lambda a, b, c: m.mhcpb_rmsnorm_backward_with_events(
-        T, H, inp["g"], inp["x"], inp["w"], wd, inp["rstd"], inp["res"], dx, dw, ws, ws.numel(),
-        sh, a, b, c)
-    call = lambda: call_ev(None, None, None)
+    n_sets = max(1, args.buffer_sets)
+    sets = [(inp["g"], inp["x"], inp["res"], dx)]
+    for _ in range(n_sets - 1):
+        sets.append((inp["g"].clone(), inp["x"].clone(),
+                     inp["res"].clone() if inp["res"] is not None else None, torch.empty_like(dx)))
+    call_ev, call = cycling([
+        (lambda a, b, c, g=g, xs=xs, res=res, dxs=dxs: m.mhcpb_rmsnorm_backward_with_events(
+            T, H, g, xs, inp["w"], wd, inp["rstd"], res, dxs, dw, ws, ws.numel(), sh, a, b, c))
+        for g, xs, res, dxs in sets])
     load_kernels(args.stage)
     settle.update(device_settle(SETTLE_MS if not args.no_settle else 0))
     for _ in range(args.warmup):
@@ -623,6 +665,7 @@ def run_rmsnorm(args, wl, settle) -> dict:
                          + (", g_residual BF16" if wl.residual else "")
                          + "; dx BF16, dw FP32"),
             "stage": "rmsnorm", "T": T, "H": H, "blocks": S,
+            "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets),
             "bytes_per_call": call_bytes,
             "bytes_per_call_without_partials": io_bytes,
             "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),
@@ -660,6 +703,9 @@ def main(argv=None):
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="rows of the workload the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--buffer-sets", type=int, default=2,
+                    help="copies of the large inputs and outputs the calls cycle through "
+                         "(1: the same buffers every call)")
     ap.add_argument("--no-settle", action="store_true",
                     help="skip the ~300 ms of BF16 matrix products before the warm-up")
     ap.add_argument("--form", choices=("fused", "split"), default="fused",
@@ -738,10 +784,17 @@ def main(argv=None):
         print(json.dumps(out), flush=True)
         return 0
     stream = torch.cuda.current_stream()
-    call_ev = lambda a, b, c: mhcpb_execute_with_events(
-        plan.handle, inp["x"], inp["w"], inp["grad_proj"], inp["grad_r"], inp["r"], dx, dw,
-        inp.get("addend"), ws, ws.numel(), stream.cuda_stream, a, b, c)
-    call = lambda: call_ev(None, None, None)
+    n_sets = max(1, args.buffer_sets)
+    sets = [(inp["x"], inp.get("addend"), dx)]
+    for _ in range(n_sets - 1):
+        ad = inp.get("addend")
+        sets.append((inp["x"].clone(), ad.clone() if ad is not None else None,
+                     torch.empty_like(dx)))
+    call_ev, call = cycling([
+        (lambda a, b, c, xs=xs, ad=ad, dxs=dxs: mhcpb_execute_with_events(
+            plan.handle, xs, inp["w"], inp["grad_proj"], inp["grad_r"], inp["r"], dxs, dw,
+            ad, ws, ws.numel(), stream.cuda_stream, a, b, c))
+        for xs, ad, dxs in sets])
     load_kernels(args.stage)
     settle.update(device_settle(SETTLE_MS if not args.no_settle else 0))
     for _ in range(args.warmup):
@@ -773,8 +826,10 @@ def main(argv=None):
                          f"{wl.hidden} (K={K}); X/W/grad_proj/grad_r/r FP32, dX BF16, "
                          f"dW FP32" + (", BF16 addend" if wl.addend else "")),
             "T": T, "K": K, "splits": S,
+            "partial_slabs_moved": partial_slabs_moved(K, S),
+            "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets),
             "bytes_per_call": call_bytes,
-            "bytes_per_call_without_partials": call_bytes - 2 * S * 24 * K * 4,
+            "bytes_per_call_without_partials": call_bytes - 2 * partial_slabs_moved(K, S) * 24 * K * 4,
             "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),
             "timed_wall_s": round(wall, 4),
             "device_settle": settle,

@@ -44,7 +44,10 @@ namespace {
 #define MHCPB_X_AUX 2
 #endif
 // Cache policy of the dX stores (written once, read by a later stage):
-// non-temporal as well.
+// non-temporal as well.  Write-through stores (sc1) are faster only while the
+// whole dX fits the 256 MB Infinity Cache and the next call rewrites the same
+// buffer (T = 4096, one buffer: 87 against 92 us per call); with the buffers
+// rotated, or at T = 16384, they are 2-5 % slower.
 #ifndef MHCPB_DX_AUX
 #define MHCPB_DX_AUX 2
 #endif

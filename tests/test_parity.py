@@ -135,3 +135,28 @@ def test_max_hidden_sampled():
     _check_dw(gh.host(dw)[:, cols], gh.host_cols(inp, cols), L, S, "max hidden")
     assert bool(torch.isfinite(dx.float()).all().item())
     assert bool(torch.isfinite(dw).all().item())
+
+
+@pytest.mark.parametrize("T,hidden", [(600, 20480), (1300, 20800)])
+def test_single_slab_group_sampled(T, hidden):
+    """K >= 256 * 320 columns: the column tiles alone fill 256 CUs, so one slab
+    group walks every slab of its tile and stores only their running sum (the
+    whole ascending sum); kernel 2 then starts from the last slab.  Sampled
+    dX rows (every column) and dW columns (every row), several whole tiles."""
+    wl = workloads.custom(T, 4, hidden, seed=T + hidden, rescale_rows=True)
+    print(f"T={wl.T} K={wl.K}", flush=True)
+    inp = workloads.make(wl, "cuda")
+    dx, dw, ws, plan = gh.run(inp)
+    S = mhcpb_plan_split_count(plan.handle)
+    assert S == 8
+    L = -(-wl.T // S)
+    rng = np.random.default_rng(wl.seed)
+    rows = gh.sample_rows(wl.T, L, rng, extra=8)
+    cols = gh.sample_cols(wl.K, rng, extra=24, whole_first=640)
+    h = gh.host_rows(inp, rows)
+    dx_rows = gh.bf16_bits_np(dx.index_select(0, torch.as_tensor(rows, device="cuda")))
+    _check_dx(dx_rows, h, wl.K, f"T={T} hidden={hidden}")
+    _check_dw(gh.host(dw)[:, cols], gh.host_cols(inp, cols), L, S, f"T={T} hidden={hidden}",
+              exact_cols=48)
+    assert bool(torch.isfinite(dx.float()).all().item())
+    assert bool(torch.isfinite(dw).all().item())
