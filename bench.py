@@ -50,23 +50,14 @@ TRACE_FILE = os.path.join(ROOT, "profiles", "projection_train_kernel_stats.json"
 SETTLE_MS = 300.0
 
 
-def partial_slabs_moved(K: int, S: int) -> int:
-    """Workspace slabs that kernel 1 writes and kernel 2 reads: S, less the
-    ones kernel 1's slab group 0 adds up before it stores them (its run of
-    S // G consecutive slabs leaves one).  G follows kernel 1's launch shape:
-    320-column tiles, min(S, 256 // tiles) slab groups, at least one."""
-    tiles = -(-K // 320)
-    groups = max(1, min(S, 256 // tiles))
-    return S - (S // groups - 1)
-
-
-def algorithmic_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
+def algorithmic_bytes(T: int, K: int, moved: int, addend: bool) -> tuple[int, int]:
     """(whole call, kernel 1) algorithmic bytes: X read and dX written once
-    (and the addend read), W, P, grad_r and r read, the partial slabs moved
-    written by kernel 1 and read by kernel 2, and dW written."""
+    (and the addend read), W, P, grad_r and r read, the `moved` partial slabs
+    (mhcpb_plan_partial_slabs) written by kernel 1 and read by kernel 2, and
+    dW written."""
     big = T * K * 4 + T * K * 2 + (T * K * 2 if addend else 0)
     small = 24 * K * 4 + 24 * T * 4 + 2 * T * 4
-    slabs = partial_slabs_moved(K, S) * 24 * K * 4
+    slabs = moved * 24 * K * 4
     k1 = big + small + slabs
     call = k1 + slabs + 24 * K * 4
     return call, k1
@@ -300,7 +291,7 @@ def _row_chunks(rows: int, parts: int):
     return [(a, min(rows, a + step)) for a in range(0, rows, step)]
 
 
-def cpu_baseline(inp, rows: int, T: int, K: int, S: int, addend: bool):
+def cpu_baseline(inp, rows: int, T: int, K: int, moved: int, addend: bool):
     """Time the FP64 oracle (as it is) on the first `rows` rows of the
     workload, dX rows and their dW contribution, on every host core the
     process may use (one thread per core, rows split into equal chunks);
@@ -322,7 +313,7 @@ def cpu_baseline(inp, rows: int, T: int, K: int, S: int, addend: bool):
     dt1 = threaded_oracle(work, [(0, one_rows)], 1)
     cores = _oracle_threads()
     dt = threaded_oracle(work, _row_chunks(rows, cores), cores)
-    call_bytes, _ = algorithmic_bytes(T, K, S, addend)
+    call_bytes, _ = algorithmic_bytes(T, K, moved, addend)
     return {
         "value": round(call_bytes * (rows / T) / dt / 1e9, 6),
         "unit": "GB/s",
@@ -337,17 +328,17 @@ def cpu_baseline(inp, rows: int, T: int, K: int, S: int, addend: bool):
     }
 
 
-def split_bytes(T: int, K: int, S: int, addend: bool) -> tuple[int, int]:
+def split_bytes(T: int, K: int, moved: int, addend: bool) -> tuple[int, int]:
     """Algorithmic bytes of (mhcpb_execute_dx, mhcpb_execute_dw) calls."""
     dx = T * K * 4 + T * K * 2 + (T * K * 2 if addend else 0) + 24 * K * 4 + 24 * T * 4 + 2 * T * 4
-    dw = T * K * 4 + 24 * T * 4 + 2 * partial_slabs_moved(K, S) * 24 * K * 4 + 24 * K * 4
+    dw = T * K * 4 + 24 * T * 4 + 2 * moved * 24 * K * 4 + 24 * K * 4
     return dx, dw
 
 
 def run_split(args, wl, inp, plan, S, dx, dw, ws, settle) -> dict:
     """The split form: per step the dX-only call then the dW-only call."""
     import torch
-    from rms_backward_amd import mhcpb_execute_dw, mhcpb_execute_dx
+    from rms_backward_amd import mhcpb_execute_dw, mhcpb_execute_dx, mhcpb_plan_partial_slabs
     T, K = wl.T, wl.K
     stream = torch.cuda.current_stream()
     h = plan.handle
@@ -376,7 +367,7 @@ def run_split(args, wl, inp, plan, S, dx, dw, ws, settle) -> dict:
     wall = time.perf_counter() - t0
     dx_us = timed(call_dx, args.steps)
     dw_us = timed(call_dw, args.steps)
-    dx_bytes, dw_bytes = split_bytes(T, K, S, wl.addend)
+    dx_bytes, dw_bytes = split_bytes(T, K, mhcpb_plan_partial_slabs(plan.handle), wl.addend)
     gbps = (dx_bytes + dw_bytes) / (us_per_step * 1e-6) / 1e9
     dx_gbps = dx_bytes / (dx_us * 1e-6) / 1e9
     return {
@@ -734,7 +725,8 @@ def main(argv=None):
         return 0
 
     import workloads
-    from rms_backward_amd import mhcpb_execute_with_events, mhcpb_plan_split_count
+    from rms_backward_amd import (mhcpb_execute_with_events, mhcpb_plan_partial_slabs,
+                                  mhcpb_plan_split_count)
     from rms_backward_amd.wrapper import Plan
     from tests import gpu_harness as gh
 
@@ -778,7 +770,8 @@ def main(argv=None):
         out = run_split(args, wl, inp, plan, S, dx, dw, ws, settle)
         if not args.no_cpu_baseline:
             print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
-            out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, T, K, S, wl.addend)
+            out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, T, K, mhcpb_plan_partial_slabs(plan.handle),
+                                          wl.addend)
         else:
             out["cpu_baseline"] = None
         print(json.dumps(out), flush=True)
@@ -804,7 +797,8 @@ def main(argv=None):
     # kernel durations: the event pass right after
     k1, k2 = event_pass(call_ev, max(args.steps, 100))
 
-    call_bytes, k1_bytes = algorithmic_bytes(T, K, S, wl.addend)
+    moved = mhcpb_plan_partial_slabs(plan.handle)
+    call_bytes, k1_bytes = algorithmic_bytes(T, K, moved, wl.addend)
     gbps = call_bytes / (us_per_call * 1e-6) / 1e9
     out = {
         "metric": METRIC,
@@ -826,10 +820,10 @@ def main(argv=None):
                          f"{wl.hidden} (K={K}); X/W/grad_proj/grad_r/r FP32, dX BF16, "
                          f"dW FP32" + (", BF16 addend" if wl.addend else "")),
             "T": T, "K": K, "splits": S,
-            "partial_slabs_moved": partial_slabs_moved(K, S),
+            "partial_slabs_moved": moved,
             "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets),
             "bytes_per_call": call_bytes,
-            "bytes_per_call_without_partials": call_bytes - 2 * partial_slabs_moved(K, S) * 24 * K * 4,
+            "bytes_per_call_without_partials": call_bytes - 2 * moved * 24 * K * 4,
             "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),
             "timed_wall_s": round(wall, 4),
             "device_settle": settle,
@@ -839,7 +833,8 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, T, K, S, wl.addend)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, T, K, mhcpb_plan_partial_slabs(plan.handle),
+                                          wl.addend)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -85,6 +85,18 @@ mhcpb_status_t mhcpb_workspace_bytes(mhcpb_plan_t plan, size_t *bytes);
 mhcpb_status_t mhcpb_plan_split_count(mhcpb_plan_t plan, int32_t *splits);
 
 /*
+ * The number of partial dW slabs an execute() call of the plan writes to the
+ * workspace and reads back (for byte accounting): S, less the slabs whose
+ * sum kernel 1 forms before it stores them.  Kernel 1's workgroups walk runs
+ * of consecutive slabs; the one that holds slabs 0 .. n-1 of a column tile
+ * adds their partials up in ascending order, as kernel 2 would, and stores
+ * only the sum (in slab n - 1, where kernel 2 then starts), so n - 1 slabs
+ * are neither written nor read.  n depends on the launch shape (T and K), never
+ * on the device; dW bits do not depend on it.  Host work only.
+ */
+mhcpb_status_t mhcpb_plan_partial_slabs(mhcpb_plan_t plan, int32_t *slabs);
+
+/*
  * Enqueue the stage on `stream` (0 = the null stream): kernel 1 streams X
  * once, writes dX and one partial dW slab per split into the workspace;
  * kernel 2 sums the slabs in ascending split order into dW.

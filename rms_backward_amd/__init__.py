@@ -38,7 +38,8 @@ MHCPB_ERROR_LAUNCH = 6
 
 EXPORTED = (
     "mhcpb_plan_create", "mhcpb_plan_destroy", "mhcpb_workspace_bytes",
-    "mhcpb_plan_split_count", "mhcpb_execute", "mhcpb_execute_with_events",
+    "mhcpb_plan_split_count", "mhcpb_plan_partial_slabs", "mhcpb_execute",
+    "mhcpb_execute_with_events",
     "mhcpb_execute_noalloc", "mhcpb_execute_dx", "mhcpb_execute_dw", "mhcpb_status_string",
     "mhcpb_forward_workspace_bytes", "mhcpb_forward", "mhcpb_forward_with_events",
     "mhcpb_rmsnorm_backward_workspace_bytes", "mhcpb_rmsnorm_backward",
@@ -58,6 +59,8 @@ _lib.mhcpb_workspace_bytes.argtypes = [_vp, ctypes.POINTER(ctypes.c_size_t)]
 _lib.mhcpb_workspace_bytes.restype = ctypes.c_int
 _lib.mhcpb_plan_split_count.argtypes = [_vp, ctypes.POINTER(ctypes.c_int32)]
 _lib.mhcpb_plan_split_count.restype = ctypes.c_int
+_lib.mhcpb_plan_partial_slabs.argtypes = [_vp, ctypes.POINTER(ctypes.c_int32)]
+_lib.mhcpb_plan_partial_slabs.restype = ctypes.c_int
 _EXEC_ARGS = [_vp] * 10 + [ctypes.c_size_t, _vp]
 _lib.mhcpb_execute.argtypes = _EXEC_ARGS
 _lib.mhcpb_execute.restype = ctypes.c_int
@@ -141,6 +144,14 @@ def mhcpb_plan_split_count(plan: int) -> int:
     st = _lib.mhcpb_plan_split_count(plan, ctypes.byref(n))
     if st != MHCPB_SUCCESS:
         raise MhcpbError(st, "mhcpb_plan_split_count")
+    return n.value
+
+
+def mhcpb_plan_partial_slabs(plan: int) -> int:
+    n = ctypes.c_int32()
+    st = _lib.mhcpb_plan_partial_slabs(plan, ctypes.byref(n))
+    if st != MHCPB_SUCCESS:
+        raise MhcpbError(st, "mhcpb_plan_partial_slabs")
     return n.value
 
 

@@ -29,6 +29,50 @@ inline int32_t split_count(int64_t T) {
     return static_cast<int32_t>(s > kMaxSplits ? kMaxSplits : s);
 }
 
+// Launch shape of kernel 1, a performance choice only (each column's dW is
+// summed over the same rows in the same order whatever the shape, so no bit
+// depends on it): compute waves per workgroup (64 columns each), column
+// tiles, slab groups (workgroups per tile, each walking a run of consecutive
+// slabs), and the slab in which slab group 0 leaves the sum of its slabs,
+// where kernel 2 starts.
+struct ProjShape {
+    int32_t nw;
+    int32_t tiles;
+    int32_t groups;
+    int32_t first_slab;
+};
+
+// Workgroups kernel 1 aims at: one per CU of a 256-CU GPU.
+constexpr int32_t kTargetWorkgroups = 256;
+
+// Five compute waves per workgroup (320-column tiles, one workgroup per CU)
+// unless that leaves more than half of the 256 CUs without a workgroup; then
+// one compute wave (64-column tiles, up to three workgroups per CU), provided
+// every workgroup still walks a single slab.  Measured on MI355X over shapes
+// from T = 64 to 16384 and K = 1200 to 16384: one-wave workgroups are 17-30 %
+// faster where five-wave ones fill at most 104 CUs, and up to twice as slow
+// where they fill 128 or more, or where a one-wave workgroup would walk two
+// slabs.  Slab groups: as many as keep the grid within 256 workgroups (five
+// waves), at least one and at most S.
+inline ProjShape projection_shape(int64_t K, int32_t S) {
+    ProjShape sh{};
+    const int64_t tiles5 = (K + 319) / 320;
+    const int64_t tiles1 = (K + 63) / 64;
+    if (tiles5 * S < kTargetWorkgroups / 2 && tiles1 * S <= 3 * kTargetWorkgroups) {
+        sh.nw = 1;
+        sh.tiles = static_cast<int32_t>(tiles1);
+        sh.groups = S;
+    } else {
+        sh.nw = 5;
+        sh.tiles = static_cast<int32_t>(tiles5);
+        const int64_t g = kTargetWorkgroups / tiles5;
+        sh.groups = static_cast<int32_t>(g < 1 ? 1 : (g > S ? S : g));
+    }
+    // Group 0 walks slabs [0, S / groups).
+    sh.first_slab = S / sh.groups - 1;
+    return sh;
+}
+
 struct Plan {
     int64_t T;
     int32_t streams;
@@ -38,6 +82,7 @@ struct Plan {
     int64_t L;        // rows per slab, ceil(T / S); the last slab may be shorter
     size_t ws_bytes;  // S * 24 * K * 4
     int32_t wait_polls;  // bound of the kernels' LDS counter waits
+    ProjShape shape;  // launch shape of kernel 1
 };
 
 // Default bound of the kernels' LDS counter waits (polls of a few dozen
@@ -68,8 +113,9 @@ enum class Outputs { kBoth, kDxOnly, kDwOnly };
 // optional events take the start and end times of the dispatch.
 hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop);
-// Kernel 2: dW = sum of the S slabs in ascending order; the optional event
-// takes the end time of the dispatch.
+// Kernel 2: dW = sum of the S slabs in ascending order (from the slab in
+// which kernel 1's slab group 0 left the sum of its slabs); the optional
+// event takes the end time of the dispatch.
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop);
 
 // The static workspace of mhcpb_execute_noalloc: kStaticWorkspaceBytes of

@@ -175,7 +175,7 @@ struct StepCursor {
 
 // First slab of slab group sg: the G groups split the S slabs into runs of
 // consecutive slabs, as even as they can be (G <= S, so none is empty).
-__host__ __device__ __forceinline__ int group_first_slab(int sg, int S, int G) {
+__device__ __forceinline__ int group_first_slab(int sg, int S, int G) {
     return static_cast<int>((static_cast<int64_t>(sg) * S) / G);
 }
 
@@ -209,9 +209,6 @@ __device__ __forceinline__ bool cursor_next(StepCursor &c, int64_t L, int64_t T)
 
 // Number of store instructions of one partial dW write (per compute wave).
 constexpr int kPartialStores = 6;
-
-// Compute waves per kernel-1 workgroup (64 columns each).
-constexpr int kProjectionWaves = 5;
 
 // The producer's writes of j = pj0 + E and pj0 + E + 1 (E even) of one row
 // into the dX operand: pa_hi points at the row's part 0 entry of j = pj0.
@@ -846,22 +843,11 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_slabs(const float *__re
     reinterpret_cast<f32x4 *>(dw)[i] = a;
 }
 
-// Slab groups G of kernel 1: enough workgroups (tiles x G) for one per CU of
-// a 256-CU GPU where the tiles allow it, never more groups than slabs.  A
-// performance choice only: no bit of the result depends on it.
-constexpr int kTargetWorkgroups = 256;
-inline int slab_groups(int tiles, int S) {
-    int G = kTargetWorkgroups / (tiles > 0 ? tiles : 1);
-    if (G > S) G = S;
-    return G < 1 ? 1 : G;
-}
-
 template <int NW>
 hipError_t launch_projection_t(const Plan &p, const Args &a, Outputs out, hipStream_t stream,
                                hipEvent_t start, hipEvent_t stop) {
-    constexpr int cols = NW * 64;
-    const int tiles = static_cast<int>((p.K + cols - 1) / cols);
-    const int G = slab_groups(tiles, p.S);
+    const int tiles = p.shape.tiles;
+    const int G = p.shape.groups;
     const dim3 grid(static_cast<unsigned>(tiles) * static_cast<unsigned>(G));
     const dim3 block((NW + 1) * kWave);
 #define MHCPB_LAUNCH(ADD, DX, DW)                                                               \
@@ -888,27 +874,31 @@ hipError_t launch_projection_t(const Plan &p, const Args &a, Outputs out, hipStr
 
 }  // namespace
 
-// Launch shape, a performance choice only: each column's dW is summed in the
-// same order whatever the workgroup width or slab grouping, so every shape
-// gives the same bits.  Five compute waves and the producer per workgroup, one
-// workgroup per CU; at K = 20480 with 8 splits, 64 column tiles x 4 slab
-// groups fill 256 CUs once.
+// Launch shape (the plan's, a performance choice only): five compute waves
+// and the producer per workgroup, one workgroup per CU (at K = 20480 with 8
+// splits, 64 column tiles x 4 slab groups fill 256 CUs once); one compute
+// wave per workgroup for narrow problems, which would otherwise leave most
+// CUs idle.
 hipError_t launch_projection(const Plan &p, const Args &a, Outputs out, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
-    return launch_projection_t<kProjectionWaves>(p, a, out, stream, start, stop);
+    switch (p.shape.nw) {
+    case 5:
+        return launch_projection_t<5>(p, a, out, stream, start, stop);
+    case 1:
+        return launch_projection_t<1>(p, a, out, stream, start, stop);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_reduce(const Plan &p, const Args &a, hipStream_t stream, hipEvent_t stop) {
-    // The column tiles of kernel 1 (kProjectionWaves * 64 columns each).
-    constexpr int tile_quads = kProjectionWaves * kWave / 4;
-    const int tiles = static_cast<int>((p.K + 4 * tile_quads - 1) / (4 * tile_quads));
+    // The column tiles of kernel 1 (nw * 64 columns each).
+    const int tile_quads = p.shape.nw * kWave / 4;
+    const int tiles = p.shape.tiles;
     const int64_t per_xcd = static_cast<int64_t>((tiles + kXcds - 1) / kXcds) * kProjCols * tile_quads;
     const unsigned blocks =
         static_cast<unsigned>(kXcds * ((per_xcd + kReduceThreads - 1) / kReduceThreads));
-    // Slab group 0 of kernel 1 leaves the sum of its slabs in its last one.
-    const int first = group_first_slab(1, p.S, slab_groups(tiles, p.S)) - 1;
     return launch(reduce_slabs, dim3(blocks), dim3(kReduceThreads), stream, nullptr, stop, a.ws,
-                  a.dw, first, p.S, p.K, tile_quads, tiles);
+                  a.dw, p.shape.first_slab, p.S, p.K, tile_quads, tiles);
 }
 
 // Static workspace for callers that cannot allocate (mhcpb_execute_noalloc).

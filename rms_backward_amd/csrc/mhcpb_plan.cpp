@@ -225,6 +225,7 @@ mhcpb_status_t mhcpb_plan_create(mhcpb_plan_t *plan, int64_t T, int32_t streams,
     p.L = (T + p.S - 1) / p.S;
     p.ws_bytes = static_cast<size_t>(p.S) * mhcpb::kProjCols * static_cast<size_t>(p.K) * 4;
     p.wait_polls = wait_polls_setting();
+    p.shape = mhcpb::projection_shape(p.K, p.S);
     auto *h = new (std::nothrow) mhcpb_plan_s{p};
     if (!h)
         return MHCPB_ERROR_INVALID_ARGUMENT;
@@ -248,6 +249,13 @@ mhcpb_status_t mhcpb_plan_split_count(mhcpb_plan_t plan, int32_t *splits) {
     if (!plan || !splits)
         return MHCPB_ERROR_INVALID_ARGUMENT;
     *splits = plan->plan.S;
+    return MHCPB_SUCCESS;
+}
+
+mhcpb_status_t mhcpb_plan_partial_slabs(mhcpb_plan_t plan, int32_t *slabs) {
+    if (!plan || !slabs)
+        return MHCPB_ERROR_INVALID_ARGUMENT;
+    *slabs = plan->plan.S - plan->plan.shape.first_slab;
     return MHCPB_SUCCESS;
 }
 

@@ -46,6 +46,32 @@ def test_workspace_at_supported_profile_matches_page():
         m.mhcpb_plan_destroy(plan)
 
 
+@pytest.mark.parametrize("T,hidden,moved", [
+    # 64 tiles of 320 columns x 8 slabs: 4 slab groups of 2; group 0 stores
+    # only the sum of slabs 0 and 1.
+    (4096, 5120, 7),
+    # 32 slabs in 4 groups of 8: group 0 leaves one of its 8.
+    (16384, 5120, 25), (65536, 5120, 25),
+    # 256 tiles alone fill the GPU: one group walks all 8 slabs.
+    (4096, 20480, 1),
+    # tiny: 32 tiles of 64 columns x 8 slabs, one slab per group.
+    (512, 512, 8),
+    # 9 slabs in 4 groups of 2, 2, 2 and 3: group 0 stores the sum of 0 and 1.
+    (4097, 5120, 8),
+    # 16 or 30 tiles of 320 columns, 8 groups of one slab.
+    (1024, 1280, 8), (4096, 2400, 8),
+    # one slab: nothing to fold.
+    (40, 1 << 20, 1), (16, 64, 1),
+])
+def test_partial_slabs_moved(T, hidden, moved):
+    plan = m.mhcpb_plan_create(T, 4, hidden)
+    try:
+        assert m.mhcpb_plan_partial_slabs(plan) == moved
+        assert 1 <= moved <= m.mhcpb_plan_split_count(plan)
+    finally:
+        m.mhcpb_plan_destroy(plan)
+
+
 @pytest.mark.parametrize("T,expect", [(1, 1), (64, 1), (65, 2), (300, 5), (448, 7), (449, 8),
                                       (511, 8), (512, 8), (513, 8), (4095, 8), (4096, 8),
                                       (4097, 9), (16383, 32), (16384, 32), (65536, 32),

@@ -20,30 +20,17 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_stage_bytes_at_the_supported_profile():
-    T, K, S = 4096, 20480, 8
-    # 64 column tiles of 320 on 256 CUs: 4 slab groups of 2 consecutive slabs;
-    # group 0 stores the sum of slabs 0 and 1 only, so 7 of the 8 slabs move.
-    assert bench.partial_slabs_moved(K, S) == 7
-    call, k1 = bench.algorithmic_bytes(T, K, S, False)
+    T, K = 4096, 20480
+    # 7 of the 8 slabs move at this profile (mhcpb_plan_partial_slabs; see
+    # tests/test_abi.py).
+    call, k1 = bench.algorithmic_bytes(T, K, 7, False)
     x, dx = T * K * 4, T * K * 2
     small = 24 * K * 4 + 24 * T * 4 + 2 * T * 4   # W, P columns 0..23, grad_r and r
     slabs = 7 * 24 * K * 4
     assert k1 == x + dx + small + slabs == 519471104
     assert call == k1 + slabs + 24 * K * 4 == 535199744
-    call_a, k1_a = bench.algorithmic_bytes(T, K, S, True)
+    call_a, k1_a = bench.algorithmic_bytes(T, K, 7, True)
     assert k1_a - k1 == T * K * 2 and call_a - call == T * K * 2   # the BF16 addend
-
-
-def test_partial_slabs_moved_at_other_shapes():
-    # 256 tiles fill the GPU alone: one slab group walks all slabs and
-    # stores only their sum.
-    assert bench.partial_slabs_moved(256 * 320, 8) == 1
-    # Tiny: 7 tiles, 8 slabs, 8 groups of one slab: nothing to fold.
-    assert bench.partial_slabs_moved(2048, 8) == 8
-    # One tile and 32 slabs: 32 groups of one slab.
-    assert bench.partial_slabs_moved(320, 32) == 32
-    # 64 tiles and 32 slabs: 4 groups of 8, group 0 leaves one of its 8.
-    assert bench.partial_slabs_moved(20480, 32) == 25
 
 
 def test_forward_and_rmsnorm_bytes():

@@ -160,3 +160,31 @@ def test_single_slab_group_sampled(T, hidden):
               exact_cols=48)
     assert bool(torch.isfinite(dx.float()).all().item())
     assert bool(torch.isfinite(dw).all().item())
+
+
+def test_one_wave_workgroups_several_per_cu_every_element():
+    """K = 3200 at 8 slabs: 320-column tiles would fill 80 CUs, so kernel 1
+    runs 400 one-wave workgroups (50 tiles of 64 columns x 8 slabs), more
+    than one per CU.  Every element against the oracle."""
+    test_small_shapes_every_element(4096, 800, True, True)
+
+
+def test_uneven_slab_groups_sampled():
+    """T = 4097: 9 slabs in 4 slab groups of 2, 2, 2 and 3 consecutive slabs;
+    group 0 adds slabs 0 and 1 up before storing them."""
+    wl = workloads.custom(4097, 4, 5120, seed=4097 + 5120, rescale_rows=True)
+    print(f"T={wl.T} K={wl.K}", flush=True)
+    inp = workloads.make(wl, "cuda")
+    dx, dw, ws, plan = gh.run(inp)
+    S = mhcpb_plan_split_count(plan.handle)
+    assert S == 9
+    L = -(-wl.T // S)
+    rng = np.random.default_rng(wl.seed)
+    rows = gh.sample_rows(wl.T, L, rng, extra=8)
+    cols = gh.sample_cols(wl.K, rng, extra=24, whole_first=640)
+    h = gh.host_rows(inp, rows)
+    dx_rows = gh.bf16_bits_np(dx.index_select(0, torch.as_tensor(rows, device="cuda")))
+    _check_dx(dx_rows, h, wl.K, "T=4097")
+    _check_dw(gh.host(dw)[:, cols], gh.host_cols(inp, cols), L, S, "T=4097", exact_cols=48)
+    assert bool(torch.isfinite(dx.float()).all().item())
+    assert bool(torch.isfinite(dw).all().item())
