@@ -152,8 +152,9 @@ mhcpb_status_t mhcpb_execute_with_events(
  * 64 MiB (67,108,864 bytes) per GPU that the library holds from its load
  * until the process ends; the call allocates nothing.  Arguments, results and
  * errors are those of mhcpb_execute, plus MHCPB_ERROR_WORKSPACE when the
- * plan's workspace (mhcpb_workspace_bytes) exceeds 64 MiB (T > 16384 at
- * K = 20480) and MHCPB_ERROR_LAUNCH when the static workspace cannot be
+ * plan's workspace (mhcpb_workspace_bytes, S * 24 * K * 4) exceeds 64 MiB
+ * (every T fits at K = 20480; with 32 slabs, T > 15872, K must stay within
+ * 21,845) and MHCPB_ERROR_LAUNCH when the static workspace cannot be
  * located on the current device.  The device is the calling thread's current
  * one (hipGetDevice), which must be the device of `stream` and the buffers.
  * Every such call on one GPU shares that workspace: calls that overlap in
