@@ -76,11 +76,25 @@ def cycling(calls_ev):
     return call_ev, (lambda: call_ev(None, None, None))
 
 
-def buffer_sets_note(n: int) -> str:
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def buffer_sets(requested: int, set_bytes: int) -> int:
+    """Buffer sets the calls cycle through: `requested`, or by default (0) as
+    many as make the sets' large buffers at least twice the 256 MB Infinity
+    Cache (two at least), so that no call finds data of an earlier call in
+    that cache."""
+    if requested > 0:
+        return requested
+    return max(2, -(-2 * INFINITY_CACHE_BYTES // max(1, set_bytes)))
+
+
+def buffer_sets_note(n: int, set_bytes: int) -> str:
     if n <= 1:
         return "one set of inputs and outputs, the same buffers every call"
-    return (f"the calls cycle through {n} copies of the large inputs and outputs, so that no "
-            f"call finds the previous call's data in the 256 MB Infinity Cache")
+    return (f"the calls cycle through {n} copies of the large inputs and outputs "
+            f"({n * set_bytes / 1e6:.0f} MB in all), so that no call finds the data of an "
+            f"earlier call in the 256 MB Infinity Cache")
 
 
 def source_hash(paths) -> str:
@@ -390,7 +404,7 @@ def run_split(args, wl, inp, plan, S, dx, dw, ws, settle) -> dict:
                          f"{wl.hidden} (K={K}); split form (dX call, then dW call)"
                          + (", BF16 addend" if wl.addend else "")),
             "form": "split", "T": T, "K": K, "splits": S,
-            "buffer_sets": 1, "buffers": buffer_sets_note(1),
+            "buffer_sets": 1, "buffers": buffer_sets_note(1, 0),
             "bytes_per_step": dx_bytes + dw_bytes,
             "dx_call_bytes": dx_bytes, "dw_call_bytes": dw_bytes,
             "dx_call_us": round(dx_us, 2), "dw_call_us": round(dw_us, 2),
@@ -477,7 +491,8 @@ def run_forward(args, wl, settle) -> dict:
     ws = plan.alloc_forward_workspace("cuda")
     eps = 1e-6
     stream = torch.cuda.current_stream()
-    n_sets = max(1, args.buffer_sets)
+    set_bytes = T * K * 4
+    n_sets = buffer_sets(args.buffer_sets, set_bytes)
     xsets = [x] + [x.clone() for _ in range(n_sets - 1)]
     call_ev, call = cycling([
         (lambda a, b, c, xs=xs: mhcpb_forward_with_events(plan.handle, xs, w, eps, proj, r, ws,
@@ -513,7 +528,7 @@ def run_forward(args, wl, settle) -> dict:
             "workload": (f"{wl.name} forward: T={T} tokens, {wl.streams} streams x hidden "
                          f"{wl.hidden} (K={K}); X, W FP32 in, proj [T, 32] and r FP32 out"),
             "stage": "forward", "T": T, "K": K,
-            "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets),
+            "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets, set_bytes),
             "bytes_per_call": call_bytes,
             "bytes_per_call_without_partials": io_bytes,
             "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),
@@ -614,7 +629,8 @@ def run_rmsnorm(args, wl, settle) -> dict:
                      device="cuda")
     wd = m.MHCPB_DTYPE_F32 if wl.w_f32 else m.MHCPB_DTYPE_BF16
     sh = torch.cuda.current_stream().cuda_stream
-    n_sets = max(1, args.buffer_sets)
+    set_bytes = T * H * 2 * (3 + (1 if wl.residual else 0))
+    n_sets = buffer_sets(args.buffer_sets, set_bytes)
     sets = [(inp["g"], inp["x"], inp["res"], dx)]
     for _ in range(n_sets - 1):
         sets.append((inp["g"].clone(), inp["x"].clone(),
@@ -656,7 +672,7 @@ def run_rmsnorm(args, wl, settle) -> dict:
                          + (", g_residual BF16" if wl.residual else "")
                          + "; dx BF16, dw FP32"),
             "stage": "rmsnorm", "T": T, "H": H, "blocks": S,
-            "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets),
+            "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets, set_bytes),
             "bytes_per_call": call_bytes,
             "bytes_per_call_without_partials": io_bytes,
             "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),
@@ -682,6 +698,27 @@ def run_copy_calibration(nbytes: int, reps: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def workload_by_name(name: str):
+    """A workload of the stage named T<T>_s4_h<hidden> (the naming of
+    workloads.custom), beside the named ones."""
+    import re
+    import workloads
+    m = re.fullmatch(r"T(\d+)_s4_h(\d+)", name)
+    if not m:
+        raise SystemExit(f"bench.py: unknown workload {name!r}")
+    return workloads.custom(int(m.group(1)), 4, int(m.group(2)))
+
+
+def rms_workload_by_name(name: str):
+    """An RMSNorm workload named rms_T<T>_H<H> (workloads.rms_custom)."""
+    import re
+    import workloads
+    m = re.fullmatch(r"rms_T(\d+)_H(\d+)", name)
+    if not m:
+        raise SystemExit(f"bench.py: unknown RMSNorm workload {name!r}")
+    return workloads.rms_custom(int(m.group(1)), int(m.group(2)))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -694,9 +731,10 @@ def main(argv=None):
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="rows of the workload the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--buffer-sets", type=int, default=2,
-                    help="copies of the large inputs and outputs the calls cycle through "
-                         "(1: the same buffers every call)")
+    ap.add_argument("--buffer-sets", type=int, default=0,
+                    help="copies of the large inputs and outputs the calls cycle through (1: "
+                         "the same buffers every call; default: enough that they total twice "
+                         "the 256 MB Infinity Cache, at least 2)")
     ap.add_argument("--no-settle", action="store_true",
                     help="skip the ~300 ms of BF16 matrix products before the warm-up")
     ap.add_argument("--form", choices=("fused", "split"), default="fused",
@@ -733,7 +771,7 @@ def main(argv=None):
     settle = {}
     if args.stage == "rmsnorm":
         name = "rms_train" if args.workload == "train" else args.workload
-        wl = workloads.RMS_WORKLOADS[name]
+        wl = workloads.RMS_WORKLOADS.get(name) or rms_workload_by_name(name)
         print(f"bench: workload {wl.name} T={wl.T} H={wl.H} stage rmsnorm", file=sys.stderr,
               flush=True)
         out = run_rmsnorm(args, wl, settle)
@@ -746,7 +784,7 @@ def main(argv=None):
         print(json.dumps(out), flush=True)
         return 0
 
-    wl = workloads.WORKLOADS[args.workload]
+    wl = workloads.WORKLOADS.get(args.workload) or workload_by_name(args.workload)
     T, K = wl.T, wl.K
     print(f"bench: workload {wl.name} T={T} K={K} stage {args.stage}", file=sys.stderr,
           flush=True)
@@ -777,7 +815,8 @@ def main(argv=None):
         print(json.dumps(out), flush=True)
         return 0
     stream = torch.cuda.current_stream()
-    n_sets = max(1, args.buffer_sets)
+    set_bytes = T * K * 4 + T * K * 2 + (T * K * 2 if wl.addend else 0)
+    n_sets = buffer_sets(args.buffer_sets, set_bytes)
     sets = [(inp["x"], inp.get("addend"), dx)]
     for _ in range(n_sets - 1):
         ad = inp.get("addend")
@@ -821,7 +860,7 @@ def main(argv=None):
                          f"dW FP32" + (", BF16 addend" if wl.addend else "")),
             "T": T, "K": K, "splits": S,
             "partial_slabs_moved": moved,
-            "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets),
+            "buffer_sets": n_sets, "buffers": buffer_sets_note(n_sets, set_bytes),
             "bytes_per_call": call_bytes,
             "bytes_per_call_without_partials": call_bytes - 2 * moved * 24 * K * 4,
             "k1_us": round(sum(k1) / len(k1), 2), "k2_us": round(sum(k2) / len(k2), 2),

@@ -83,14 +83,8 @@ struct alignas(16) StepP {
 
 // Operand slots in rotation, and how many steps ahead of its conversion the
 // producer requests the raw P of a step.
-#ifndef MHCPB_SLOTS
-#define MHCPB_SLOTS 4
-#endif
-#ifndef MHCPB_RAW_AHEAD
-#define MHCPB_RAW_AHEAD 2
-#endif
-constexpr int kSlots = MHCPB_SLOTS;
-constexpr int kRawAhead = MHCPB_RAW_AHEAD;
+constexpr int kSlots = 4;
+constexpr int kRawAhead = 2;
 constexpr int kRawBufs = kRawAhead + 1;
 
 // Kernel 1.  A workgroup has NW compute waves, which own the NW * 64 columns
@@ -795,20 +789,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
 // round-robin by index and the tile count is a multiple of 8 (the supported
 // profile), so that the slabs stored last are still in that XCD's L2.  Any
 // other placement gives the same sums, only slower.
-#ifndef MHCPB_K2_NT
-#define MHCPB_K2_NT 1
-#endif
 constexpr int kReduceBatch = 8;
 constexpr int kXcds = 8;
-#ifndef MHCPB_K2_THREADS
-#define MHCPB_K2_THREADS 256
-#endif
-constexpr int kReduceThreads = MHCPB_K2_THREADS;
+constexpr int kReduceThreads = 256;
 __device__ __forceinline__ f32x4 load_slab_quad(const f32x4 *p) {
-    if constexpr (MHCPB_K2_NT)
-        return __builtin_nontemporal_load(p);
-    else
-        return *p;
+    return __builtin_nontemporal_load(p);
 }
 __global__ __launch_bounds__(kReduceThreads) void reduce_slabs(const float *__restrict__ ws,
                                                                float *__restrict__ dw, int first,
