@@ -1,14 +1,16 @@
 // Kernels of the DSv4.1 mHC projection/RMS backward for gfx950.
 //
-// Kernel 1 ("projection"): the grid is (column tiles) x (S slabs of T).  Each
-// workgroup owns one slab of rows and one tile of columns, reads its rows of X
-// exactly once, writes the matching dX, and keeps its dW[24, tile] partial in
-// MFMA accumulators; the partial goes to workspace slab s (one writer per
-// element).  Kernel 2 ("reduce"): dW = ((slab 0 + slab 1) + slab 2) + ... in
-// FP32.  This follows the page's structure (the token reduction split over
-// independent blocks, partial weight gradients, then a second reduction
-// kernel: "Source attribution" section) with a split count that depends on T
-// only.
+// Kernel 1 ("projection"): T is cut into S slabs (S a function of T only)
+// and K into column tiles; the grid is (column tiles) x (slab groups), each
+// workgroup walking a run of consecutive slabs of its tile.  For each slab it
+// reads the slab's rows of X exactly once, writes the matching dX, and keeps
+// the slab's dW[24, tile] partial in MFMA accumulators; the partial goes to
+// workspace slab s (one writer per element), except that the workgroups
+// holding slabs 0, 1, ... add theirs up first, in that order, and store the
+// sum.  Kernel 2 ("reduce"): dW = ((slab 0 + slab 1) + slab 2) + ... in FP32,
+// starting from that sum.  This follows the page's structure (the token
+// reduction split over independent blocks, partial weight gradients, then a
+// second reduction kernel: "Source attribution" section).
 //
 // Both products run on v_mfma_f32_16x16x32_bf16.  A TF32 operand has 11
 // significant bits; it splits exactly into a BF16 high part (its upper 16
