@@ -348,3 +348,25 @@ def test_non_finite_inputs_stay_local():
     assert len(mt.dx_violations(got_dx[fin], ref_dx[fin], np.abs(ref_dx[fin]).max())) == 0
     finw = np.isfinite(ref_dw)
     assert mt.rel_frobenius(got_dw[finw], ref_dw[finw]) < 1e-5
+
+
+@pytest.mark.parametrize("T,hidden", [(4096, 5120), (4097, 5120), (512, 512), (600, 20480)])
+def test_workspace_slabs_written_match_partial_slab_count(T, hidden):
+    """Kernel 1 writes exactly mhcpb_plan_partial_slabs of the S workspace
+    slabs: the slab group holding slabs 0 .. n-1 of each column tile stores
+    only their sum, in slab n - 1, and never touches slabs 0 .. n - 2.  The
+    workspace is prefilled with all-ones words (NaN); written slabs hold the
+    finite partials."""
+    from rms_backward_amd import mhcpb_plan_partial_slabs, mhcpb_plan_split_count
+    wl = workloads.custom(T, 4, hidden, seed=T + 3 * hidden)
+    inp = workloads.make(wl, "cuda")
+    dx, dw, ws, plan = gh.run(inp)
+    S = mhcpb_plan_split_count(plan.handle)
+    moved = mhcpb_plan_partial_slabs(plan.handle)
+    slabs = ws.view(torch.int32)[: S * 24 * wl.K].view(S, 24 * wl.K)
+    untouched = [bool((slabs[s] == -1).all().item()) for s in range(S)]
+    written = [bool(torch.isfinite(slabs[s].view(torch.float32)).all().item()) for s in range(S)]
+    first = S - moved
+    assert untouched == [s < first for s in range(S)]
+    assert written == [s >= first for s in range(S)]
+    assert bool(torch.isfinite(dw).all().item())
