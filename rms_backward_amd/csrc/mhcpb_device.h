@@ -98,53 +98,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void *base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kRsrcWord3);
 }
 
-// LDS reads the compiler does not track.  X in LDS was written by LDS DMA,
-// whose completion the caller establishes with an explicit vmcnt wait; the
-// compiler cannot see that, and would otherwise wait for every outstanding
-// global load before any LDS read it cannot prove independent of the DMA.
-// All hot-loop LDS reads therefore go through these, followed by one
-// explicit lgkmcnt wait.  The template argument is a constant byte offset
-// that goes into the instruction's offset field (no address arithmetic).
+// LDS accesses the compiler does not track.  X in LDS was written by LDS
+// DMA, whose completion the caller establishes with an explicit vmcnt wait;
+// the compiler cannot see that, and would otherwise wait for every
+// outstanding global load before any LDS read it cannot prove independent of
+// the DMA.  The hot loops therefore read LDS in asm statements of their own,
+// each of which ends with the wait for its reads (the destination of an asm
+// load holds no value the compiler may use until a wait in the same
+// statement has passed), and write it through the helpers below.  The
+// template argument is a constant byte offset that goes into the
+// instruction's offset field (no address arithmetic).
 #define MHCPB_LDS_OFFSET_CHECK static_assert(kOff >= 0 && kOff < 65536, "LDS offset field")
-template <int kOff = 0>
-__device__ __forceinline__ f32x4 lds_read_b128(uint32_t addr) {
-    MHCPB_LDS_OFFSET_CHECK;
-    f32x4 v;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
-    return v;
-}
-
-template <int kOff = 0>
-__device__ __forceinline__ u32x4 lds_read_u128(uint32_t addr) {
-    MHCPB_LDS_OFFSET_CHECK;
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
-    return v;
-}
-
-template <int kOff = 0>
-__device__ __forceinline__ uint32_t lds_read_u32(uint32_t addr) {
-    MHCPB_LDS_OFFSET_CHECK;
-    uint32_t v;
-    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
-    return v;
-}
-
-template <int kOff = 0>
-__device__ __forceinline__ float lds_read_f32(uint32_t addr) {
-    MHCPB_LDS_OFFSET_CHECK;
-    float v;
-    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
-    return v;
-}
-
-template <int kOff = 0>
-__device__ __forceinline__ u32x2 lds_read_u64(uint32_t addr) {
-    MHCPB_LDS_OFFSET_CHECK;
-    u32x2 v;
-    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOff));
-    return v;
-}
 
 // LDS writes of the operand staging and the counters, equally hidden from the
 // compiler's LDS-DMA ordering (they never touch the X ring); a wave waits for
@@ -198,6 +162,13 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // Barrier for LDS data only (no wait on outstanding global traffic).
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One LDS word, read and waited for in the same asm statement.
+__device__ __forceinline__ uint32_t lds_load_u32(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
 }
 
 // Adds one to the LDS counter at addr once this wave's earlier LDS accesses

@@ -85,7 +85,9 @@ struct FwdSlot {
 // Untracked vector memory: the kernel counts its own requests (LDS DMA of
 // X, W loads, partial stores) in explicit vmcnt waits, so none of them may
 // make the compiler insert a wait of its own, which would not count the DMA
-// and would drain the X stream.
+// and would drain the X stream.  Loads are issued in an asm statement that
+// ends with their wait (an asm load's destination holds no value the
+// compiler may use before that).
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 rsrc_words(const void *base, int bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -93,12 +95,35 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, int bytes) {
                  __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu)),
                  __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3};
 }
-// The destination register holds no value the compiler knows of until a
-// wait that names it, in the same basic block, has passed.
-__device__ __forceinline__ f32x4 load_b128_untracked(i32x4 rs, uint32_t off) {
-    f32x4 v;
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rs));
-    return v;
+// Sixteen 16-byte loads at offsets o[0..15] of the buffer rs, then a wait for
+// every request of the wave (vmcnt(0)).
+__device__ __forceinline__ void load16_b128_wait_all(i32x4 rs, const uint32_t (&o)[16],
+                                                     f32x4 (&v)[16]) {
+    asm volatile(
+        "buffer_load_dwordx4 %0, %16, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %1, %17, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %2, %18, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %3, %19, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %4, %20, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %5, %21, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %6, %22, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %7, %23, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %8, %24, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %9, %25, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %10, %26, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %11, %27, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %12, %28, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %13, %29, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %14, %30, %32, 0 offen\n\t"
+        "buffer_load_dwordx4 %15, %31, %32, 0 offen\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
+          "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+        : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "v"(o[5]), "v"(o[6]),
+          "v"(o[7]), "v"(o[8]), "v"(o[9]), "v"(o[10]), "v"(o[11]), "v"(o[12]), "v"(o[13]),
+          "v"(o[14]), "v"(o[15]), "s"(rs)
+        : "memory");
 }
 __device__ __forceinline__ void store_b32_untracked(i32x4 rs, uint32_t off, float v) {
     asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(v), "v"(off), "s"(rs) : "memory");
@@ -190,23 +215,28 @@ __device__ __forceinline__ void fwd_load_w(const FwdCtx &c, int kt, u32x4 (&bw)[
     const int g1 = 16 + (c.n16 & 7);
 #pragma unroll
     for (int G0 = 0; G0 < NG; G0 += 4) {  // four groups (16 loads) per wait
-        f32x4 v0[4][2], v1[4][2];
+        // Load n = 4 (2 G + h) + i: i = 0 gate n16, i = 1 gate g1, at column
+        // group G0 + G, half h.
+        uint32_t off[16];
 #pragma unroll
         for (int G = 0; G < 4; ++G)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int col = colbase + 32 * (G0 + G) + 8 * c.q + 4 * h;
                 const bool in = col < c.ki;
-                v0[G][h] = load_b128_untracked(
-                    rs, offset_if(in, static_cast<uint32_t>((c.n16 * c.ki + col) * 4)));
-                v1[G][h] = load_b128_untracked(
-                    rs, offset_if(in, static_cast<uint32_t>((g1 * c.ki + col) * 4)));
+                off[4 * G + 2 * h] = offset_if(in, static_cast<uint32_t>((c.n16 * c.ki + col) * 4));
+                off[4 * G + 2 * h + 1] = offset_if(in, static_cast<uint32_t>((g1 * c.ki + col) * 4));
             }
-        asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(v0[0][0]), "+v"(v0[0][1]), "+v"(v0[1][0]), "+v"(v0[1][1]),
-                       "+v"(v0[2][0]), "+v"(v0[2][1]), "+v"(v0[3][0]), "+v"(v0[3][1]),
-                       "+v"(v1[0][0]), "+v"(v1[0][1]), "+v"(v1[1][0]), "+v"(v1[1][1]),
-                       "+v"(v1[2][0]), "+v"(v1[2][1]), "+v"(v1[3][0]), "+v"(v1[3][1])::"memory");
+        f32x4 lv[16];
+        load16_b128_wait_all(rs, off, lv);
+        f32x4 v0[4][2], v1[4][2];
+#pragma unroll
+        for (int G = 0; G < 4; ++G)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                v0[G][h] = lv[4 * G + 2 * h];
+                v1[G][h] = lv[4 * G + 2 * h + 1];
+            }
 #pragma unroll
         for (int G = 0; G < 4; ++G) {
             uint32_t p0[8], p1[8];  // hi | lo << 16
@@ -263,26 +293,38 @@ __device__ __forceinline__ void fwd_reduce(const FwdCtx &c, int i, const FwdUnit
             lds_raise_poison(c.poison, c.lane);
         const int b = col / 16, nn = col % 16;
         float v[kPairsPerWave][NW], sv[kPairsPerWave][NW];
+        // The NW waves' values of this lane's element, 2 KB apart (pairs
+        // of them 256-byte strides 0 and 8 apart), their sums of squares 64
+        // bytes apart (dword offsets 0 and 16), then the poison word (read
+        // after the slot: a wave that gave up raised it before it
+        // overwrote a slot), in one asm statement with its wait.
+        static_assert(kPairsPerWave == 1 && NW == 8, "reduction reads laid out for 8 waves");
+        const int m = 2 * c.wave + c.lane / 32;
+        const uint32_t src = fwd_slot_acc<NW>(c, slot, 0, b, 16 * (m / 4) + nn) + 4 * (m % 4);
+        const uint32_t ssrc = fwd_slot_ss<NW>(c, slot, 0, m);
+        static_assert(2 * kWave * 16 == 8 * 256 && kFwdRows * 4 == 16 * 4, "read2 strides");
+        u32x2 p[4], q[4];
+        uint32_t pois;
+        asm volatile(
+            "ds_read2st64_b32 %0, %9 offset1:8\n\t"
+            "ds_read2st64_b32 %1, %9 offset0:16 offset1:24\n\t"
+            "ds_read2st64_b32 %2, %9 offset0:32 offset1:40\n\t"
+            "ds_read2st64_b32 %3, %9 offset0:48 offset1:56\n\t"
+            "ds_read2_b32 %4, %10 offset1:16\n\t"
+            "ds_read2_b32 %5, %10 offset0:32 offset1:48\n\t"
+            "ds_read2_b32 %6, %10 offset0:64 offset1:80\n\t"
+            "ds_read2_b32 %7, %10 offset0:96 offset1:112\n\t"
+            "ds_read_b32 %8, %11\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(p[0]), "=&v"(p[1]), "=&v"(p[2]), "=&v"(p[3]), "=&v"(q[0]), "=&v"(q[1]),
+              "=&v"(q[2]), "=&v"(q[3]), "=&v"(pois)
+            : "v"(src), "v"(ssrc), "v"(c.poison)
+            : "memory");
 #pragma unroll
-        for (int j = 0; j < kPairsPerWave; ++j) {
-            const int m = 2 * (c.wave * kPairsPerWave + j) + c.lane / 32;
-            const uint32_t src = fwd_slot_acc<NW>(c, slot, 0, b, 16 * (m / 4) + nn) + 4 * (m % 4);
-            const uint32_t ssrc = fwd_slot_ss<NW>(c, slot, 0, m);
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                v[j][ww] = lds_read_f32(src + ww * (2 * kWave * 16));
-                sv[j][ww] = lds_read_f32(ssrc + ww * (kFwdRows * 4));
-            }
+        for (int ww = 0; ww < NW; ++ww) {
+            v[0][ww] = __uint_as_float(ww % 2 ? p[ww / 2].y : p[ww / 2].x);
+            sv[0][ww] = __uint_as_float(ww % 2 ? q[ww / 2].y : q[ww / 2].x);
         }
-        // The poison word is read after the slot: a wave that gave up
-        // raised it before it overwrote a slot.
-        uint32_t pois = lds_read_u32(c.poison);
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(pois)::"memory");
-#pragma unroll
-        for (int j = 0; j < kPairsPerWave; ++j)
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww)
-                asm volatile("" : "+v"(v[j][ww]), "+v"(sv[j][ww]));
         poisoned = __builtin_amdgcn_readfirstlane(pois) != 0;
         lds_signal(c.consumed + 4 * slot, c.lane);
 #pragma unroll
@@ -332,12 +374,15 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &c, bool first, uint32_t s
     else
         wait_vmcnt<kFwdDma + kStores>();
     f32x4 xv[2][2];
-#pragma unroll
-    for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) xv[G][h] = lds_read_b128(sb + rd[G][h]);
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(xv[0][0]), "+v"(xv[0][1]), "+v"(xv[1][0]), "+v"(xv[1][1])::"memory");
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(xv[0][0]), "=&v"(xv[0][1]), "=&v"(xv[1][0]), "=&v"(xv[1][1])
+        : "v"(sb + rd[0][0]), "v"(sb + rd[0][1]), "v"(sb + rd[1][0]), "v"(sb + rd[1][1])
+        : "memory");
     compiler_fence();
     fwd_issue_x(c, pre, (H + 2) % SPU, sb_next, xoff, xcol);
     compiler_fence();

@@ -226,6 +226,93 @@ __device__ __forceinline__ void put_pb(uint32_t pb0, uint32_t v) {
     lds_write_u16_hi<o + 24>(pb0, v);
 }
 
+// What a compute wave reads from LDS at the top of a step.
+struct StepRead {
+    f32x4 cc;          // RMS coefficients of rows 4g .. 4g + 3
+    u32x4 pa[3];       // dX P operands: parts 0 and 1 of j = 4g .. 4g + 3, then block 1
+    u32x4 pb[2][2];    // dW P operands [part][block]
+    f32x4 xc[4];       // the step's X, 4 rows
+    uint32_t pois;     // the workgroup's poison word
+    uint32_t ready;    // ready count of the next step's slot
+};
+
+// The LDS reads of one step as a single asm statement that ends with the
+// wait for all of them (the destination of an asm load holds no value the
+// compiler may use until a wait in the same statement has passed): the P
+// operands of the step's slot (a_c, a_pa, a_pa3, a_pb[2]; the forms without
+// dX or without dW skip theirs), then the wait for this step's X
+// (vmcnt(kVm), chosen by the caller), the four X rows at xa (64 lanes x 16
+// bytes apart), the poison word and the next slot's ready count.
+template <int kVm, bool kDX, bool kDW>
+__device__ __forceinline__ void read_step(StepRead &r, uint32_t a_c, uint32_t a_pa, uint32_t a_pa3,
+                                          uint32_t a_pb0, uint32_t a_pb1, uint32_t xa,
+                                          uint32_t a_pois, uint32_t a_ready) {
+    static_assert(kVm >= 0 && kVm < 64, "vmcnt range");
+    if constexpr (kDX && kDW) {
+        asm volatile(
+            "ds_read_b128 %0, %14\n\t"
+            "ds_read_b128 %1, %15\n\t"
+            "ds_read_b128 %2, %15 offset:%22\n\t"
+            "ds_read_b128 %3, %16\n\t"
+            "ds_read_b128 %4, %17\n\t"
+            "ds_read_b128 %5, %18\n\t"
+            "ds_read_b128 %6, %17 offset:16\n\t"
+            "ds_read_b128 %7, %18 offset:16\n\t"
+            "s_waitcnt vmcnt(%23)\n\t"
+            "ds_read_b128 %8, %19\n\t"
+            "ds_read_b128 %9, %19 offset:1024\n\t"
+            "ds_read_b128 %10, %19 offset:2048\n\t"
+            "ds_read_b128 %11, %19 offset:3072\n\t"
+            "ds_read_b32 %12, %20\n\t"
+            "ds_read_b32 %13, %21\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r.cc), "=&v"(r.pa[0]), "=&v"(r.pa[1]), "=&v"(r.pa[2]), "=&v"(r.pb[0][0]),
+              "=&v"(r.pb[0][1]), "=&v"(r.pb[1][0]), "=&v"(r.pb[1][1]), "=&v"(r.xc[0]),
+              "=&v"(r.xc[1]), "=&v"(r.xc[2]), "=&v"(r.xc[3]), "=&v"(r.pois), "=&v"(r.ready)
+            : "v"(a_c), "v"(a_pa), "v"(a_pa3), "v"(a_pb0), "v"(a_pb1), "v"(xa), "v"(a_pois),
+              "v"(a_ready), "n"(4 * kProjCols), "n"(kVm)
+            : "memory");
+    } else if constexpr (kDX) {
+        asm volatile(
+            "ds_read_b128 %0, %10\n\t"
+            "ds_read_b128 %1, %11\n\t"
+            "ds_read_b128 %2, %11 offset:%16\n\t"
+            "ds_read_b128 %3, %12\n\t"
+            "s_waitcnt vmcnt(%17)\n\t"
+            "ds_read_b128 %4, %13\n\t"
+            "ds_read_b128 %5, %13 offset:1024\n\t"
+            "ds_read_b128 %6, %13 offset:2048\n\t"
+            "ds_read_b128 %7, %13 offset:3072\n\t"
+            "ds_read_b32 %8, %14\n\t"
+            "ds_read_b32 %9, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r.cc), "=&v"(r.pa[0]), "=&v"(r.pa[1]), "=&v"(r.pa[2]), "=&v"(r.xc[0]),
+              "=&v"(r.xc[1]), "=&v"(r.xc[2]), "=&v"(r.xc[3]), "=&v"(r.pois), "=&v"(r.ready)
+            : "v"(a_c), "v"(a_pa), "v"(a_pa3), "v"(xa), "v"(a_pois), "v"(a_ready),
+              "n"(4 * kProjCols), "n"(kVm)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %10\n\t"
+            "ds_read_b128 %1, %11\n\t"
+            "ds_read_b128 %2, %10 offset:16\n\t"
+            "ds_read_b128 %3, %11 offset:16\n\t"
+            "s_waitcnt vmcnt(%15)\n\t"
+            "ds_read_b128 %4, %12\n\t"
+            "ds_read_b128 %5, %12 offset:1024\n\t"
+            "ds_read_b128 %6, %12 offset:2048\n\t"
+            "ds_read_b128 %7, %12 offset:3072\n\t"
+            "ds_read_b32 %8, %13\n\t"
+            "ds_read_b32 %9, %14\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r.pb[0][0]), "=&v"(r.pb[0][1]), "=&v"(r.pb[1][0]), "=&v"(r.pb[1][1]),
+              "=&v"(r.xc[0]), "=&v"(r.xc[1]), "=&v"(r.xc[2]), "=&v"(r.xc[3]), "=&v"(r.pois),
+              "=&v"(r.ready)
+            : "v"(a_pb0), "v"(a_pb1), "v"(xa), "v"(a_pois), "v"(a_ready), "n"(kVm)
+            : "memory");
+    }
+}
+
 template <int NW, bool kAddend, bool kDX, bool kDW>
 __global__ __launch_bounds__((NW + 1) * kWave)
 __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
@@ -319,15 +406,30 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
             const RawStep &src = praw[k % kRawBufs];
             const StepP &d = pop[slot];
             const uint32_t ra = lds_addr(&src.p[0]) + static_cast<uint32_t>((prow * kProjStride + pj0) * 4);
-            u32x2 v0 = lds_read_u64(ra), v1 = lds_read_u64<8>(ra), v2 = lds_read_u64<16>(ra);
+            u32x2 v0, v1, v2;
             float grv = 0.f, rv = 1.f;
             if constexpr (kDX) {
                 const uint32_t rl = lds_addr(&src) + 4 * lane;
-                grv = lds_read_f32<offsetof(RawStep, gr)>(rl);
-                rv = lds_read_f32<offsetof(RawStep, r)>(rl);
+                asm volatile(
+                    "ds_read_b64 %0, %5\n\t"
+                    "ds_read_b64 %1, %5 offset:8\n\t"
+                    "ds_read_b64 %2, %5 offset:16\n\t"
+                    "ds_read_b32 %3, %6 offset:%7\n\t"
+                    "ds_read_b32 %4, %6 offset:%8\n\t"
+                    "s_waitcnt lgkmcnt(0)"
+                    : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(grv), "=&v"(rv)
+                    : "v"(ra), "v"(rl), "n"(offsetof(RawStep, gr)), "n"(offsetof(RawStep, r))
+                    : "memory");
+            } else {
+                asm volatile(
+                    "ds_read_b64 %0, %3\n\t"
+                    "ds_read_b64 %1, %3 offset:8\n\t"
+                    "ds_read_b64 %2, %3 offset:16\n\t"
+                    "s_waitcnt lgkmcnt(0)"
+                    : "=&v"(v0), "=&v"(v1), "=&v"(v2)
+                    : "v"(ra)
+                    : "memory");
             }
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(grv), "+v"(rv)::"memory");
             const uint32_t vv[6] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y};
             uint32_t pk[6];  // hi | lo << 16
 #pragma unroll
@@ -489,11 +591,27 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             constexpr int kQ = 4;
             const int nq = h == 0 ? 4 : 2;
-#pragma unroll
-            for (int q = 0; q < kQ; ++q)
-                if (q < nq) tv[q] = lds_read_u128(buf + static_cast<uint32_t>(((4 * q + g) * 64 + 4 * c16) * 4));
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(tv[0]), "+v"(tv[1]), "+v"(tv[2]), "+v"(tv[3])::"memory");
+            // Rows 4 q + g, q < nq, 1 KB apart.
+            const uint32_t tb = buf + static_cast<uint32_t>((g * 64 + 4 * c16) * 4);
+            if (h == 0) {
+                asm volatile(
+                    "ds_read_b128 %0, %4\n\t"
+                    "ds_read_b128 %1, %4 offset:1024\n\t"
+                    "ds_read_b128 %2, %4 offset:2048\n\t"
+                    "ds_read_b128 %3, %4 offset:3072\n\t"
+                    "s_waitcnt lgkmcnt(0)"
+                    : "=&v"(tv[0]), "=&v"(tv[1]), "=&v"(tv[2]), "=&v"(tv[3])
+                    : "v"(tb)
+                    : "memory");
+            } else {
+                asm volatile(
+                    "ds_read_b128 %0, %2\n\t"
+                    "ds_read_b128 %1, %2 offset:1024\n\t"
+                    "s_waitcnt lgkmcnt(0)"
+                    : "=&v"(tv[0]), "=&v"(tv[1])
+                    : "v"(tb)
+                    : "memory");
+            }
             if (poisoned) {
 #pragma unroll
                 for (int q = 0; q < kQ; ++q) tv[q] = u32x4{0x7FC00000u, 0x7FC00000u, 0x7FC00000u, 0x7FC00000u};
@@ -509,9 +627,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
     StepCursor cur = cursor_start(sg, S, G, L, T);  // the step being computed
     char *d_cur = reinterpret_cast<char *>(dx + cur.row0 * K + kw);
     const char *a_cur = reinterpret_cast<const char *>(addend + cur.row0 * K + kw);
-    // The ready count of a step's slot is read one step early, so that its
-    // round trip is off the step's critical path.
-    uint32_t ready_seen = lds_read_u32(ready_addr);
+    // The ready count of a step's slot is read one step early (with the
+    // previous step's LDS reads), so that its round trip is off the step's
+    // critical path.
+    uint32_t ready_seen = lds_load_u32(ready_addr);
     // With the addend, the dX stores of a step are issued one step late,
     // right after the next X request (same bits; at T = 16384 with the
     // addend 466 against 475 us, while without it they cost about 2 us at
@@ -543,7 +662,6 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         // of the same kernel without it).
         __builtin_amdgcn_s_setprio(1);
         const int slot = k % kSlots;
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ready_seen)::"memory");
         const uint32_t want = static_cast<uint32_t>(k / kSlots + 1);
         if (__builtin_amdgcn_readfirstlane(ready_seen) < want &&
             !lds_wait_at_least(ready_addr + 4 * slot, want, max_polls)) {
@@ -553,33 +671,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         // The P operands of this step are requested first: the RMS
         // coefficients of rows 4g..4g+3, the dX P operands (token c16, part
         // p, j = 16b + 4g .. +3) and the dW P operands (part p, j = 16b +
-        // c16, rows 4g .. 4g+3; entries j >= 24 are zero).
-        f32x4 cc = {};
-        u32x4 pa[3] = {};     // parts 0 and 1 of j = 4g .. 4g + 3, then block 1
-        u32x4 pb[2][2] = {};  // [part][block]
-        const uint32_t slot_base = lds_addr(&pop[slot]);
-        if constexpr (kDX) {
-            cc = lds_read_b128(slot_base + off_c);
-            pa[0] = lds_read_u128(slot_base + off_pa);
-            pa[1] = lds_read_u128<4 * kProjCols>(slot_base + off_pa);
-            pa[2] = lds_read_u128(slot_base + off_pa3);
-        }
-        if constexpr (kDW) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                pb[0][b] = lds_read_u128(slot_base + off_pb[b]);
-                pb[1][b] = lds_read_u128<16>(slot_base + off_pb[b]);
-            }
-        }
-        // Then wait for this step's X and read it (4 rows).  Step k >= 1
-        // issues, in this order: [4 addend loads] 4 X DMA (for step k + 1),
-        // [4 dX stores of step k - 1 when deferred], [4 dX stores of step k
-        // otherwise], [the kPartialStores partial stores when step k ends a
-        // unit]; step 0 issues no X (the prologue requested steps 0 and 1,
-        // after the W loads).  So after the X of step k come at most 4 dX
-        // stores (of step k - 1, or of step k - 2 when deferred; none without
-        // dX) and, when step k - 1 ended a unit and stored its partial, those
-        // stores;
+        // c16, rows 4g .. 4g+3; entries j >= 24 are zero).  Then the wait for
+        // this step's X, and its 4 rows.  Step k >= 1 issues, in this order:
+        // [4 addend loads] 4 X DMA (for step k + 1), [4 dX stores of step
+        // k - 1 when deferred], [4 dX stores of step k otherwise], [the
+        // kPartialStores partial stores when step k ends a unit]; step 0
+        // issues no X (the prologue requested steps 0 and 1, after the W
+        // loads).  So after the X of step k come at most 4 dX stores (of step
+        // k - 1, or of step k - 2 when deferred; none without dX) and, when
+        // step k - 1 ended a unit and stored its partial, those stores;
         // after the X of step 0 the X of step 1: vmcnt(4), or vmcnt(0) for
         // the later steps of the dW-only form, plus kPartialStores after a
         // unit's end, covers it.  With deferred stores step 0 stores nothing,
@@ -587,43 +687,36 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         // step 1 with the addend, step 0's addend loads come after the X of
         // step 1 as well, and the wait is only stricter.  Steps past the slab
         // end are still requested (they read zeros; their stores fall outside
-        // the range), which keeps every step's count identical.
+        // the range), which keeps every step's count identical.  The poison
+        // word is read after the slot: a producer that gave up raised it
+        // before it overwrote a slot.
+        const uint32_t slot_base = lds_addr(&pop[slot]);
+        const uint32_t xa = ring_base + static_cast<uint32_t>((((k & 1) * 4) * kWave + lane) * 16);
+        const uint32_t a_ready = ready_addr + 4 * ((k + 1) % kSlots);
+        StepRead rd;
         const bool four = k == 0 || (kDX && !(kDefer && k == 1));
+#define MHCPB_READ_STEP(VM)                                                                     \
+    read_step<VM, kDX, kDW>(rd, slot_base + off_c, slot_base + off_pa, slot_base + off_pa3,    \
+                            slot_base + off_pb[0], slot_base + off_pb[1], xa, poison_addr,    \
+                            a_ready)
         if (!stored || !kDW) {
             if (four)
-                wait_vmcnt<4>();
+                MHCPB_READ_STEP(4);
             else
-                wait_vmcnt<0>();
+                MHCPB_READ_STEP(0);
         } else {
             if (four)
-                wait_vmcnt<4 + kPartialStores>();
+                MHCPB_READ_STEP(4 + kPartialStores);
             else
-                wait_vmcnt<kPartialStores>();
+                MHCPB_READ_STEP(kPartialStores);
         }
-        const uint32_t xa = ring_base + static_cast<uint32_t>((((k & 1) * 4) * kWave + lane) * 16);
-        f32x4 xc[4];
-        xc[0] = lds_read_b128(xa);
-        xc[1] = lds_read_b128<kWave * 16>(xa);
-        xc[2] = lds_read_b128<2 * kWave * 16>(xa);
-        xc[3] = lds_read_b128<3 * kWave * 16>(xa);
-        // The poison word is read after the slot: a producer that gave up
-        // raised it before it overwrote a slot.
-        uint32_t pois = lds_read_u32(poison_addr);
-        // The wait names every register the reads above return, so no use
-        // of them can be scheduled before the data has arrived.
-        if constexpr (kDX && kDW)
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
-                           "+v"(pa[0]), "+v"(pa[1]), "+v"(pa[2]), "+v"(pb[0][0]), "+v"(pb[0][1]),
-                           "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(pois)::"memory");
-        else if constexpr (kDX)
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(cc),
-                           "+v"(pa[0]), "+v"(pa[1]), "+v"(pa[2]), "+v"(pois)::"memory");
-        else
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(xc[0]), "+v"(xc[1]), "+v"(xc[2]), "+v"(xc[3]), "+v"(pb[0][0]),
-                           "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(pois)::"memory");
+#undef MHCPB_READ_STEP
+        const f32x4 cc = rd.cc;
+        const u32x4(&pa)[3] = rd.pa;
+        const u32x4(&pb)[2][2] = rd.pb;
+        const f32x4(&xc)[4] = rd.xc;
+        const uint32_t pois = rd.pois;
+        ready_seen = rd.ready;
         bad = bad || __builtin_amdgcn_readfirstlane(pois) != 0;
         lds_signal(consumed_addr + 4 * slot, lane);
         uint2 av[4] = {};
@@ -720,7 +813,6 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         }
         d_cur += kStepRows * row_bytes_d;
         if constexpr (kAddend) a_cur += kStepRows * row_bytes_d;
-        ready_seen = lds_read_u32(ready_addr + 4 * ((k + 1) % kSlots));
         const int s_done = cur.s;
         const bool after_unit = cursor_next(cur, L, T);
         if (after_unit) {
@@ -769,7 +861,6 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{pend[rr][0], pend[rr][1]}, prs, doff[rr],
                                                   0, MHCPB_DX_AUX);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ready_seen)::"memory");
     // Drain the X DMA still in flight (the steps past the last unit) before
     // the workgroup's LDS can be released.
     wait_vmcnt<0>();
