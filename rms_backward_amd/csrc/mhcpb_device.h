@@ -195,6 +195,12 @@ __device__ __forceinline__ bool lds_wait_at_least(uint32_t addr, uint32_t target
     return false;
 }
 
+// Lane 0 writes v to the LDS word at addr; no wait (a reader takes whatever
+// value it finds).
+__device__ __forceinline__ void lds_publish(uint32_t addr, uint32_t v, int lane) {
+    if (lane == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
 // Sets the workgroup's LDS poison word at addr (lane 0 writes it) and waits
 // until the write has completed, so that LDS accesses issued afterwards by
 // this wave come after it.
