@@ -26,8 +26,12 @@
  * The library never allocates, frees or synchronizes device memory; a plan
  * holds host metadata only ("Prepared class API" section: compile() does no
  * tensor work, execute() allocates no tensor storage and enqueues exactly two
- * kernels).  Every function returns a status and never throws; on any error
- * no kernel is launched and no output is written.
+ * kernels).  Every function returns a status and never throws.  Arguments
+ * are validated before anything is enqueued: on a validation error no kernel
+ * is launched and no output is written.  MHCPB_ERROR_LAUNCH reports a launch
+ * the runtime refused; when that is a call's second kernel, the first one is
+ * already enqueued and its outputs (dX, the workspace) are to be treated as
+ * undefined.
  */
 #ifndef MHCPB_H
 #define MHCPB_H
@@ -98,8 +102,9 @@ mhcpb_status_t mhcpb_plan_partial_slabs(mhcpb_plan_t plan, int32_t *slabs);
 
 /*
  * Enqueue the stage on `stream` (0 = the null stream): kernel 1 streams X
- * once, writes dX and one partial dW slab per split into the workspace;
- * kernel 2 sums the slabs in ascending split order into dW.
+ * once, writes dX and the partial dW slabs (mhcpb_plan_partial_slabs of the
+ * S, the first of them holding the sum of the slabs before it) into the
+ * workspace; kernel 2 sums them in ascending split order into dW.
  *
  *   x              [T, K]  FP32 input
  *   w              [24, K] FP32 projection weight
@@ -301,8 +306,8 @@ mhcpb_status_t mhcpb_rmsnorm_backward_workspace_bytes(int64_t T, int32_t H, size
  * Pointers that take part must be 16-byte aligned and their byte ranges
  * disjoint (MHCPB_ERROR_MISALIGNED, MHCPB_ERROR_OVERLAP); g, x, rstd and dx
  * may be NULL only when T = 0; w and dw are always required.  Like
- * mhcpb_execute it only validates and launches, allocates nothing, and on any
- * error launches nothing.
+ * mhcpb_execute it only validates and launches, allocates nothing, and on a
+ * validation error launches nothing.
  */
 mhcpb_status_t mhcpb_rmsnorm_backward(int64_t T, int32_t H, const uint16_t *g, const uint16_t *x,
                                       const void *w, mhcpb_dtype_t w_dtype, const float *rstd,
