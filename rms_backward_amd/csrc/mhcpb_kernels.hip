@@ -734,11 +734,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void projection_kernel(
         // level up, so that the older wave no longer wins every tie and the
         // younger one no longer ends the workgroup 2 us after the others
         // (0.4 us less per call at T = 4096, 1.6 at T = 16384; same bits).
-        // Every wave publishes the steps it has begun; a wave without a
-        // mate reads its own count, which is never ahead of it.
-        const bool behind = static_cast<int>(__builtin_amdgcn_readfirstlane(rd.mate)) > k;
+        // With five compute waves every wave publishes the steps it has
+        // begun; a wave without a mate reads its own count, which is never
+        // ahead of it (one-wave workgroups skip all of this).
+        constexpr bool kMates = NW == 5;
+        const bool behind = kMates && static_cast<int>(__builtin_amdgcn_readfirstlane(rd.mate)) > k;
         if (behind) __builtin_amdgcn_s_setprio(2);
-        lds_publish(my_prog_addr, static_cast<uint32_t>(k + 1), lane);
+        if (kMates) lds_publish(my_prog_addr, static_cast<uint32_t>(k + 1), lane);
         bad = bad || __builtin_amdgcn_readfirstlane(pois) != 0;
         lds_signal(consumed_addr + 4 * slot, lane);
         uint2 av[4] = {};
