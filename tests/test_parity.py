@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import workloads
-from rms_backward_amd import mhcpb_plan_split_count
+from rms_backward_amd import mhcpb_plan_partial_slabs, mhcpb_plan_split_count
 from tests import gpu_harness as gh
 from tests.oracle_checks import check_dw as _check_dw
 from tests.oracle_checks import check_dx as _check_dx
@@ -167,6 +167,23 @@ def test_one_wave_workgroups_several_per_cu_every_element():
     runs 400 one-wave workgroups (50 tiles of 64 columns x 8 slabs), more
     than one per CU.  Every element against the oracle."""
     test_small_shapes_every_element(4096, 800, True, True)
+
+
+@pytest.mark.parametrize("T,hidden,addend,rescale", [
+    (1000, 3000, False, True),   # K = 12000: 38 tiles of 320 columns x 8 slabs, 6 slab groups
+    (777, 2750, True, False),    # K = 11000, ragged last tile and last slab
+    (520, 5120, True, True),     # K = 20480: 4 slab groups of 2 slabs, group 0 adds its two up
+])
+def test_five_wave_workgroups_every_element(T, hidden, addend, rescale):
+    """Kernel 1 with five compute waves per workgroup (320-column tiles, one
+    workgroup per CU; the two waves that share a SIMD take turns at a raised
+    priority), every element against the oracle; at K = 20480 the workgroups
+    of slab group 0 add the partials of slabs 0 and 1 before storing them."""
+    if hidden == 5120:
+        plan = gh.Plan(T, 4, hidden)
+        assert mhcpb_plan_split_count(plan.handle) == 8
+        assert mhcpb_plan_partial_slabs(plan.handle) == 7
+    test_small_shapes_every_element(T, hidden, addend, rescale)
 
 
 def test_uneven_slab_groups_sampled():
