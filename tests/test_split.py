@@ -22,6 +22,7 @@ SMALL = [
     (17, 66, True),
     (513, 130, False),
     (2049, 34, True),
+    (520, 5120, True),   # five-wave workgroups, slab group 0 adding its partials up
 ]
 FULL = [
     # sampled rows and columns against the oracle
